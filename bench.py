@@ -1,0 +1,233 @@
+"""Benchmark of the target-verify path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload high_batch]
+
+A step is one pass of the whole path for one batch: tv_build_tree_mask,
+tv_verify_attn (prefix stream, merge with tail and chain, scratch pad),
+tv_accept and tv_refresh_state.  Inputs are seeded synthetic data resident in HBM
+before timing; the persistent state evolves from step to step as it would while
+decoding.  Prints one JSON line:
+
+  value          verified tree tokens per second (B*D per step / step time)
+  roofline       the prefix-stream attention kernel: algorithmic bytes per launch
+                 (every committed pool entry's K and V once, plus Q) over its
+                 average launch time from HIP events on its stream, vs 8 TB/s
+  cpu_baseline   the fp64 oracle timed on this host for a bounded sample of the
+                 same workload (rank 0, N = 1 only)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak (AMD's published figure)
+N_INPUT_SETS = 4        # distinct per-step input sets, rotated
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="high_batch")
+    ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library's choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_mfma.hip", "tv_common.h"):
+        with open(os.path.join(ROOT, "tree_speculative_decoding_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the prefix kernel from committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_attn_prefix_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU "
+              "in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import tree_speculative_decoding_amd as tv
+
+    w = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    B, D, Hq, Hkv, d = w.B, w.D, w.Hq, w.Hkv, w.d
+    e = 2 if w.dtype == "bf16" else 4
+    total_steps = args.warmup + args.steps
+    caps = [tv.round_cap(w.P // C + math.ceil(total_steps * D / C) + 2) for C in w.levels]
+
+    # ---- persistent state: committed compressed entries drawn directly (pooled prefix)
+    t0 = time.time()
+    st = tv.DeviceState(B, Hkv, d, w.dtype, w.levels, caps)
+    import concurrent.futures as cf
+
+    def draw(b):
+        return [(k, np.ascontiguousarray(v.transpose(0, 2, 1))) for k, v in synth.pooled_prefix(w, b)]
+
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        for b, lv in enumerate(ex.map(draw, range(B))):
+            for l, (k, vt) in enumerate(lv):
+                n = k.shape[1]
+                st.pool_k[l][b, :, :n] = tv.to_device(k, w.dtype)
+                st.pool_vt[l][b, :, :, :n] = tv.to_device(vt, w.dtype)
+                st.n[l][b] = n
+    st.P.fill_(w.P)
+
+    # ---- per-step inputs (N_INPUT_SETS sets, rotated)
+    sets = []
+    for t in range(N_INPUT_SETS):
+        s = synth.step_inputs(w, t)
+        i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+        sets.append(dict(parents=i32(s.parents), draft=i32(s.draft), target=i32(s.target),
+                         q=tv.to_device(s.q, w.dtype), kt=tv.to_device(s.k_tree, w.dtype),
+                         vt=tv.to_device(s.v_tree, w.dtype)))
+    anc = torch.zeros(B, D, dtype=torch.int64, device=dev)
+    depth = torch.zeros(B, D, dtype=torch.int32, device=dev)
+    err = torch.zeros(B, dtype=torch.int32, device=dev)
+    out = torch.zeros(B, D, Hq, d, dtype=tv.tv.torch_dtype(w.dtype), device=dev)
+    lse = torch.zeros(B, D, Hq, dtype=torch.float32, device=dev)
+    m = torch.zeros(B, dtype=torch.int32, device=dev)
+    path = torch.zeros(B, D, dtype=torch.int32, device=dev)
+    bonus = torch.zeros(B, dtype=torch.int32, device=dev)
+    log = torch.zeros(B, len(w.levels), D, 2, dtype=torch.int32, device=dev)
+    sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels))
+    ws_bytes = tv.tv_verify_attn_workspace_bytes(D, Hq, st, args.splits)
+    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def one_step(x):
+        tv.tv_build_tree_mask(x["parents"], anc, depth, err, stream)
+        tv.tv_verify_attn(x["q"], x["kt"], x["vt"], anc, depth, err, st, sc, out, lse, ws, args.splits, stream)
+        tv.tv_accept(x["parents"], anc, depth, x["draft"], x["target"], err, m, path, bonus, stream)
+        tv.tv_refresh_state(st, sc, x["kt"], x["vt"], m, path, log, err, stream)
+
+    for t in range(args.warmup):
+        one_step(sets[t % N_INPUT_SETS])
+    torch.cuda.synchronize()
+
+    # per-launch events around the prefix kernel (recorded by the library on `stream`)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in ev:  # materialise the HIP events
+        a_.record(stream)
+        b_.record(stream)
+    n_sum_before = sum(int(x.sum()) for x in st.n)
+    P_before = st.P.clone()
+    acc_len = torch.zeros(B, dtype=torch.int64, device=dev)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for t in range(args.steps):
+        tv.tv_set_timing_events(ev[t][0], ev[t][1])
+        one_step(sets[(args.warmup + t) % N_INPUT_SETS])
+    stop.record(stream)
+    tv.tv_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    attn_ms = [a_.elapsed_time(b_) for a_, b_ in ev]
+    attn_avg_ms = float(np.mean(attn_ms))
+    n_sum_after = sum(int(x.sum()) for x in st.n)
+    accepted = (st.P - P_before).double().mean().item() / args.steps  # mean m + 1 per step
+
+    # algorithmic bytes of the prefix kernel per launch: every committed entry's K and V
+    # (averaged over the timed steps as the pools grow) plus the queries
+    entries_per_seq_head = (n_sum_before + n_sum_after) / 2.0 / B
+    attn_bytes = B * Hkv * entries_per_seq_head * d * 2 * e + B * D * Hq * d * e
+    achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
+    errs = int((err != 0).sum())
+
+    result = {
+        "metric": "verified tree tokens/sec at D=8 bs=64 + achieved HBM GB/s fraction of peak",
+        "value": round(B * D / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "D": D, "Hq": Hq, "Hkv": Hkv, "head_dim": d,
+                   "prefix_tokens": w.P, "levels": list(w.levels), "tree": w.spec_name,
+                   "p_agree": w.p_agree, "splits": args.splits or "auto",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
+                     "kernel": "k_attn_mfma (prefix stream)", "avg_launch_ms": round(attn_avg_ms, 5),
+                     "algorithmic_bytes_per_launch": int(attn_bytes)},
+        "accepted_length": round(accepted, 4),
+        "seq_errors": errs,
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle, as it stands, on whole sequences of the same workload until the
+    time budget is spent (at least one); tokens/s = sequences * D / time."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    caps = [w.P // C + 64 for C in w.levels]
+    done, t_used = 0, 0.0
+    b = 0
+    while done == 0 or t_used < budget_s:
+        if b >= w.B:
+            break
+        ents = [[(oracle.widen(k, w.dtype), oracle.widen(v, w.dtype)) for k, v in synth.pooled_prefix(w, b)]]
+        ost = oracle.from_entries(ents, [w.P], w.levels, caps, w.d)
+        s = synth.step_inputs(w, 0, batch=[b])
+        q, kt, vt = (oracle.widen(a, w.dtype) for a in (s.q, s.k_tree, s.v_tree))
+        t0 = time.perf_counter()
+        oracle.step(ost, s.parents, s.draft, s.target, q, kt, vt)
+        t_used += time.perf_counter() - t0
+        done += 1
+        b += 1
+    return {"value": round(done * w.D / t_used, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences of {w.name}, one full step each (plan, attention, scratch, "
+                      f"accept, refresh), fp64 numpy; input widening excluded; {t_used:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

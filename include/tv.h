@@ -1,0 +1,222 @@
+/*
+ * tv.h — C ABI of the target-verify path of tree-structured speculative decoding
+ * over sequence-compressed attention KV, for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: "Adapting Tree-Structured Speculative Decoding to
+ * DeepSeek-V4 for Efficient Inference" (cited TSD-V4; that page has no numbered
+ * headings, section numbers are inferred from its own "Sec. 5.2/5.3" references
+ * and the order of its topics).  One decoding step of the path is:
+ *
+ *   tv_build_tree_mask   verify preprocess: tree -> verification plan      (§4.1)
+ *   tv_verify_attn       branch-aware causal attention + per-chain scratch  (§3.1, §4.1, §4.2)
+ *   tv_accept            accepted-path selection                            (§3.1, §4.4)
+ *   tv_refresh_state     accepted-path refresh of the compressed state      (§3.2, §4.2, §4.3)
+ *
+ * plus tv_compress_prefix, which builds the compressed state of a raw prefix.
+ *
+ * Conventions
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer after a call returns.  The
+ *    tv_state / tv_scratch structs themselves are host structs passed by address;
+ *    they are read during the call only.
+ *  - Every call is asynchronous on `stream`; none synchronises the device or
+ *    allocates, so the four-call step can be captured in a hipGraph.
+ *  - Host-checkable argument errors return TV_EINVAL / TV_EUNSUPPORTED /
+ *    TV_EWORKSPACE before anything is launched (device memory untouched);
+ *    tv_last_error() then describes the problem.  Launch failures return TV_EHIP.
+ *  - Data-dependent errors are per sequence, in seq_err[b] (TV_SEQ_*): a
+ *    sequence with a nonzero code is skipped by every later call of the step and
+ *    its persistent state is left unchanged.
+ *  - D counts the tree's root.  Node 0 is the root: the last committed token,
+ *    whose K/V is computed by this verify and is not yet in the state.  Nodes are
+ *    in topological order: parents[0] = -1 and 0 <= parents[i] < i.  D <= 64.
+ *  - A node's position is P + depth(node), P = committed length of its sequence.
+ *  - Element types: TV_BF16 (bfloat16) or TV_F32, the same for Q, tree K/V, pools,
+ *    tail, scratch entries and the attention output.  Open-block sums, the LSE and
+ *    all accumulation are fp32.
+ *  - Compression stand-in (the pages leave CSA/HCA's compressor undefined): level
+ *    l with block size C keeps one entry per complete aligned block [jC, jC+C) of
+ *    committed positions, the unweighted mean of its K (and of its V) per KV head.
+ */
+#ifndef TV_H
+#define TV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define TV_API __attribute__((visibility("default")))
+#else
+#define TV_API
+#endif
+
+#define TV_VERSION 100      /* 1.0.0 */
+#define TV_MAX_LEVELS 2
+#define TV_MAX_D 64
+#define TV_POOL_ALIGN 64    /* every pool capacity must be a multiple of this */
+
+typedef enum {
+  TV_OK = 0,
+  TV_EINVAL = -1,        /* bad argument (null pointer, size out of range, ...) */
+  TV_EUNSUPPORTED = -2,  /* valid but not implemented (e.g. head dim other than 64/128) */
+  TV_EWORKSPACE = -3,    /* workspace smaller than tv_verify_attn_workspace_bytes() */
+  TV_EHIP = -4           /* a HIP launch failed */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* seq_err codes (int32, one per sequence) */
+enum {
+  TV_SEQ_OK = 0,
+  TV_SEQ_BAD_PARENT = 1,  /* parents[b] is not a topologically ordered tree */
+  TV_SEQ_POOL_FULL = 2,   /* committing would exceed a pool's capacity */
+  TV_SEQ_BAD_PREFIX = 3,  /* tv_compress_prefix: P[b] outside [0, max_len] */
+  TV_SEQ_BAD_PATH = 4     /* tv_refresh_state: m or a path node out of range, or P < 0 */
+};
+
+/* One compression level (the pages' C4 / C128 compressed states, TSD-V4 §2.2, §4.3). */
+typedef struct {
+  int32_t C;        /* block size: tokens per compressed entry (>= 1) */
+  int32_t cap;      /* pool capacity in entries, a multiple of TV_POOL_ALIGN */
+  void* k;          /* [B][Hkv][cap][d]  committed entries, row-major (entry-major) */
+  void* vt;         /* [B][Hkv][d][cap]  committed entries, TRANSPOSED (entry index fastest) */
+  int32_t* n;       /* [B] committed entries of each sequence (kept equal to P/C) */
+  float* open_k;    /* [B][Hkv][d] fp32 sum of the committed tokens of the open block */
+  float* open_v;    /* [B][Hkv][d] */
+} tv_level;
+
+/* Persistent compressed state of B sequences (TSD-V4 §4.2 "persistent context"). */
+typedef struct {
+  int32_t B, Hkv, d;
+  int32_t dtype;                /* tv_dtype */
+  int32_t n_levels;             /* 0..TV_MAX_LEVELS, finest (smallest C) first, C strictly increasing */
+  tv_level lvl[TV_MAX_LEVELS];
+  void* tail_k;                 /* [B][Hkv][lvl[0].C-1][d] raw tokens of the finest level's open */
+  void* tail_v;                 /*   block: positions floor(P/C0)*C0 .. P-1 (may be NULL if C0 == 1) */
+  int32_t* P;                   /* [B] committed length */
+} tv_state;
+
+/* Per-branch temporary compression results (TSD-V4 §4.2 scratch pad), per level l:
+ * entry for node i is valid only if node i closes a block of that level, i.e.
+ * (P + depth(i) + 1) % C == 0; open sums are the open block after node i along
+ * its own chain (zero where it closes).  Overwritten by every tv_verify_attn. */
+typedef struct {
+  void* entry_k[TV_MAX_LEVELS];   /* [B][D][Hkv][d] element dtype */
+  void* entry_v[TV_MAX_LEVELS];   /* [B][D][Hkv][d] */
+  float* open_k[TV_MAX_LEVELS];   /* [B][D][Hkv][d] fp32 */
+  float* open_v[TV_MAX_LEVELS];   /* [B][D][Hkv][d] */
+} tv_scratch;
+
+/*
+ * Verify preprocess (TSD-V4 §4.1: the tree becomes a verification plan describing
+ * the candidate chains and their compression boundaries; §4.3: this metadata is
+ * prepared on the device).
+ *   parents  [B][D] int32 in
+ *   anc      [B][D] uint64 out: bit j of anc[b][i] set iff node j is an ancestor of
+ *            node i or i itself (the chain of node i)
+ *   depth    [B][D] int32 out: depth(i), root = 0
+ *   seq_err  [B] int32 out: TV_SEQ_OK, or TV_SEQ_BAD_PARENT (then anc = depth = 0)
+ * B >= 0 (B == 0 is a no-op), 1 <= D <= 64.
+ */
+TV_API tv_status tv_build_tree_mask(int B, int D, const int32_t* parents, uint64_t* anc,
+                                    int32_t* depth, int32_t* seq_err, hipStream_t stream);
+
+/*
+ * Bytes of device workspace tv_verify_attn needs for this state shape, with
+ * num_splits split-KV partitions (0 = the library's choice for the current device;
+ * the same value must then be passed to tv_verify_attn).  Returns 0 on invalid
+ * arguments.
+ */
+TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_splits);
+
+/*
+ * Branch-aware causal verification (TSD-V4 §3.1: each candidate attends to the
+ * accepted context and to the ancestors on its own branch only; §4.1 target
+ * verify) plus chain-wise compression into the scratch pad (§4.1: branches are
+ * compressed independently after they diverge; §4.2: temporary states stay in
+ * the scratch pad until acceptance).
+ *
+ * For node i, query head h (KV head g = h / (Hq/Hkv)) the visible rows are: every
+ * committed entry of every level (n[l][b] of them), the finest level's tail
+ * (P mod C0 raw tokens), and the tree nodes j with bit j of anc[b][i] set.  One
+ * softmax over all of them with scale 1/sqrt(d); rows not visible are never read.
+ *   q        [B][D][Hq][d]  in      k_tree, v_tree [B][D][Hkv][d] in
+ *   anc, depth from tv_build_tree_mask; seq_err [B] in (NULL = all OK)
+ *   scratch  out (NULL = do not build it); out [B][D][Hq][d] out (element dtype)
+ *   lse      [B][D][Hq] fp32 out, natural-log softmax normaliser (NULL = not wanted)
+ *   workspace: >= tv_verify_attn_workspace_bytes(D, Hq, st, num_splits) bytes
+ * Supported: d in {64, 128}; Hq % Hkv == 0; TV_BF16 with d = 128 runs the MFMA
+ * kernel, everything else the fp32 vector kernel.
+ */
+TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree,
+                                const void* v_tree, const uint64_t* anc, const int32_t* depth,
+                                const int32_t* seq_err, const tv_state* st,
+                                const tv_scratch* scratch, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, int num_splits,
+                                hipStream_t stream);
+
+/*
+ * Accepted-path selection (TSD-V4 §3.1: the result is a specific path through the
+ * tree; §4.4 accepted-path selection).  Greedy rule: draft node i >= 1 is correct
+ * iff draft_tok[i] == target_tok[parent(i)] (target_tok[u] = the target model's
+ * greedy token after node u); a node is accepted iff every node of its chain below
+ * the root is correct.  The path ends at the deepest accepted node, smallest index
+ * among equals.
+ *   m      [B] out: accepted draft tokens (= depth of the path's last node)
+ *   path   [B][D] out: path nodes root first, -1 after index m
+ *   bonus  [B] out: target_tok of the path's last node (the next step's root)
+ * Sequences with seq_err != 0 get m = -1, path = -1, bonus = -1.
+ */
+TV_API tv_status tv_accept(int B, int D, const int32_t* parents, const uint64_t* anc,
+                           const int32_t* depth, const int32_t* draft_tok,
+                           const int32_t* target_tok, const int32_t* seq_err, int32_t* m,
+                           int32_t* path, int32_t* bonus, hipStream_t stream);
+
+/*
+ * Accepted-path refresh (TSD-V4 §3.2: token history, cache and compressed states
+ * must describe the same prefix; §4.2: only the accepted path's states update the
+ * persistent state, rejected branches are dropped; §4.3 C4/C128 state updates).
+ * The root and path[1..m] become committed tokens at positions P..P+m; P' = P+m+1.
+ * For each level, every block j with floor(P/C) <= j < floor(P'/C) takes the
+ * scratch entry of the path node at its last position; the open sums become the
+ * path leaf's scratch open sums; the tail becomes positions floor(P'/C0)*C0..P'-1.
+ *   st: updated in place (pools, n, open sums, tail, P)
+ *   commit_log [B][n_levels][D][2] int32 out: rows (destination slot, source node),
+ *              -1 padded (NULL = not wanted)
+ *   seq_err [B] in/out: skipped if nonzero; set to TV_SEQ_POOL_FULL (state untouched)
+ *              if a level would exceed its capacity, TV_SEQ_BAD_PATH if m >= D or a
+ *              path node is outside 0..D-1 (state untouched)
+ */
+TV_API tv_status tv_refresh_state(int D, const tv_state* st, const tv_scratch* scratch,
+                                  const void* k_tree, const void* v_tree, const int32_t* m,
+                                  const int32_t* path, int32_t* commit_log, int32_t* seq_err,
+                                  hipStream_t stream);
+
+/*
+ * Compressed state of a raw committed prefix (TSD-V4 §2.2: compression along the
+ * sequence axis at several granularities).  Reads P[b] (set by the caller) and
+ * the raw tokens raw_k/raw_v [B][Hkv][max_len][d]; writes every level's entries
+ * 0..P/C-1, n = P/C, open sums and the tail.  seq_err[b] [B] out: TV_SEQ_OK,
+ * TV_SEQ_BAD_PREFIX (P outside [0, max_len]) or TV_SEQ_POOL_FULL.
+ */
+TV_API tv_status tv_compress_prefix(const tv_state* st, const void* raw_k, const void* raw_v,
+                                    int max_len, int32_t* seq_err, hipStream_t stream);
+
+/* Optional timing hook: when both events are non-NULL, later tv_verify_attn calls
+ * on this host thread record `start` just before and `stop` just after the
+ * prefix-streaming attention kernel, on the call's stream.  NULL, NULL turns it off. */
+TV_API tv_status tv_set_timing_events(hipEvent_t start, hipEvent_t stop);
+
+TV_API const char* tv_status_string(tv_status s);
+TV_API const char* tv_last_error(void);   /* this thread's last argument/launch error */
+TV_API int tv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TV_H */

@@ -1,0 +1,111 @@
+"""CPU checks of the C ABI: libtv.so loads, exports every function include/tv.h
+declares, and rejects invalid arguments on the host (before any launch, so these
+calls touch no GPU)."""
+import ctypes
+
+import pytest
+
+import tree_speculative_decoding_amd as tv
+from tree_speculative_decoding_amd.tv import TvScratch, TvState
+
+
+def test_library_exports_every_declared_symbol():
+    L = tv.lib()
+    names = tv.header_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert tv.tv_version() == 100
+
+
+def test_struct_layout_matches_header():
+    # tv_level: 2 x int32 + 5 pointers; tv_state: 5 x int32, 2 levels, 3 pointers
+    assert ctypes.sizeof(tv.tv.TvLevel) == 48
+    assert ctypes.sizeof(TvState) == 144
+    assert TvState.lvl.offset == 24 and TvState.P.offset == 136
+    assert ctypes.sizeof(TvScratch) == 64
+
+
+def fake_state(**kw):
+    s = TvState()
+    s.B, s.Hkv, s.d, s.dtype, s.n_levels = 2, 2, 128, 1, 2
+    for l, C in enumerate((4, 128)):
+        s.lvl[l].C, s.lvl[l].cap = C, 128
+        for f in ("k", "vt", "n", "open_k", "open_v"):
+            setattr(s.lvl[l], f, 0x1000)
+    s.tail_k = s.tail_v = s.P = 0x1000
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def status(f, *a):
+    return f(*a)
+
+
+P = ctypes.c_void_p(0x1000)
+
+
+def test_tree_mask_rejects_bad_sizes():
+    L = tv.lib()
+    assert L.tv_build_tree_mask(2, 0, P, P, P, P, None) == tv.TV_EINVAL
+    assert L.tv_build_tree_mask(2, 65, P, P, P, P, None) == tv.TV_EINVAL
+    assert L.tv_build_tree_mask(-1, 8, P, P, P, P, None) == tv.TV_EINVAL
+    assert L.tv_build_tree_mask(2, 8, None, P, P, P, None) == tv.TV_EINVAL
+    assert b"NULL" in L.tv_last_error()
+    assert L.tv_build_tree_mask(0, 8, None, None, None, None, None) == tv.TV_OK  # B = 0: nothing to do
+
+
+def test_accept_rejects_bad_sizes():
+    L = tv.lib()
+    assert L.tv_accept(4, 70, P, P, P, P, P, None, P, P, P, None) == tv.TV_EINVAL
+    assert L.tv_accept(4, 8, P, P, P, P, None, None, P, P, P, None) == tv.TV_EINVAL
+
+
+@pytest.mark.parametrize("mut,code", [
+    (dict(d=96), tv.TV_EUNSUPPORTED),
+    (dict(dtype=7), tv.TV_EINVAL),
+    (dict(n_levels=3), tv.TV_EINVAL),
+    (dict(Hkv=0), tv.TV_EINVAL),
+    (dict(P=None), tv.TV_EINVAL),
+    (dict(tail_k=None), tv.TV_EINVAL),
+])
+def test_verify_rejects_bad_state(mut, code):
+    L = tv.lib()
+    s = fake_state(**mut)
+    r = L.tv_verify_attn(8, 16, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, 1 << 30, 1, None)
+    assert r == code, tv.lib().tv_last_error()
+
+
+def test_verify_rejects_bad_levels_and_workspace():
+    L = tv.lib()
+    s = fake_state()
+    s.lvl[1].C = 4  # not increasing
+    assert L.tv_verify_attn(8, 16, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, 1 << 30, 1, None) == tv.TV_EINVAL
+    s = fake_state()
+    s.lvl[0].cap = 100  # not a multiple of 64
+    assert L.tv_verify_attn(8, 16, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, 1 << 30, 1, None) == tv.TV_EINVAL
+    s = fake_state()
+    assert L.tv_verify_attn(8, 15, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, 1 << 30, 1, None) == tv.TV_EINVAL  # Hq % Hkv
+    need = L.tv_verify_attn_workspace_bytes(8, 16, ctypes.byref(s), 3)
+    # 2 seq x 2 heads x 3 splits x 64 rows x (128 + 2) floats, each part rounded to 256 B
+    assert need == 2 * 2 * 3 * 64 * 128 * 4 + 2 * 2 * 3 * 64 * 8
+    assert L.tv_verify_attn(8, 16, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, need - 1, 3, None) == tv.TV_EWORKSPACE
+    assert L.tv_verify_attn_workspace_bytes(0, 16, ctypes.byref(s), 3) == 0
+
+
+def test_refresh_and_compress_reject_bad_args():
+    L = tv.lib()
+    s = fake_state()
+    assert L.tv_refresh_state(8, ctypes.byref(s), None, P, P, P, P, None, P, None) == tv.TV_EINVAL  # no scratch
+    sc = TvScratch()
+    assert L.tv_refresh_state(8, ctypes.byref(s), ctypes.byref(sc), P, P, P, P, None, P, None) == tv.TV_EINVAL
+    assert L.tv_compress_prefix(ctypes.byref(s), P, P, -1, P, None) == tv.TV_EINVAL
+    assert L.tv_compress_prefix(ctypes.byref(s), None, P, 10, P, None) == tv.TV_EINVAL
+    assert L.tv_set_timing_events(P, None) == tv.TV_EINVAL
+
+
+def test_status_strings():
+    L = tv.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.tv_status_string(code)

@@ -1,0 +1,139 @@
+"""GPU parity of tv_refresh_state (and the whole four-call step) against the oracle over
+many steps: acceptance, paths, commit logs, counts and tails bit-exact; compressed
+entries and open sums within tolerance; the refreshed state equals compressing the
+committed history from scratch; rejected branches never reach the state."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from harness import (Runner, check_attention, compare_state, device_state, host_f64, oracle_state, pooled_caps,
+                     upload_step, widen_step)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+MULTI = {
+    "bf16_c4_c128": (synth.Workload("ms1", 3, 8, 16, 2, 128, "bf16", (4, 128), 125, 2, 3, 0.8, 3001, prefix="raw"), 45),
+    "f32_c4_c16": (synth.Workload("ms2", 4, 7, 8, 2, 64, "f32", (4, 16), 13, 2, 3, 0.6, 3002, prefix="raw"), 40),
+    "bf16_linear": (synth.Workload("ms3", 2, 8, 16, 2, 128, "bf16", (4, 128), 250, 1, 7, 0.9, 3003, prefix="raw"), 30),
+    "bf16_c1_c4": (synth.Workload("ms4", 2, 6, 8, 1, 128, "bf16", (1, 4), 9, 2, 3, 0.7, 3004, prefix="raw"), 25),
+}
+
+
+@pytest.mark.parametrize("name", list(MULTI))
+def test_multistep_against_oracle(name):
+    import torch
+    w, T = MULTI[name]
+    _say(f"multistep {name}: {T} steps")
+    caps = pooled_caps(w, T * w.D + 8)
+    dst = device_state(w, caps, poison=True)
+    ost = oracle_state(w, caps)
+    hist_k = [oracle.widen(synth.raw_prefix(w, b)[0], w.dtype) for b in range(w.B)]
+    hist_v = [oracle.widen(synth.raw_prefix(w, b)[1], w.dtype) for b in range(w.B)]
+    r = Runner(dst, w.D, w.Hq)
+    for t in range(T):
+        s = synth.step_inputs(w, t)
+        h = widen_step(s, w.dtype)
+        x = upload_step(s, w.dtype)
+        r.step(x)
+        torch.cuda.synchronize()
+        ref = oracle.step(ost, s.parents, s.draft, s.target, h.q, h.kt, h.vt)
+        assert (r.err.cpu().numpy() == ref.err).all()
+        assert (r.m.cpu().numpy() == ref.m).all(), f"step {t}"
+        assert (r.path.cpu().numpy() == ref.path).all()
+        assert (r.bonus.cpu().numpy() == ref.bonus).all()
+        L = len(w.levels)
+        assert (r.log.cpu().numpy()[:, :L] == ref.commit_log).all(), f"step {t} commit log"
+        check_attention(host_f64(r.out, w.dtype), ref.out, w.dtype)
+        ost = ref.state
+        compare_state(dst, ost, w.dtype, f"step {t}")
+        for b in range(w.B):
+            acc = ref.path[b, :ref.m[b] + 1]
+            hist_k[b] = np.concatenate([hist_k[b], h.kt[b, acc].transpose(1, 0, 2)], axis=1)
+            hist_v[b] = np.concatenate([hist_v[b], h.vt[b, acc].transpose(1, 0, 2)], axis=1)
+    # the device state after T steps equals compressing the committed history from scratch
+    fresh = oracle.from_scratch(hist_k, hist_v, w.levels, caps)
+    compare_state(dst, fresh, w.dtype, "from scratch")
+
+
+def test_rejected_branches_never_reach_state():
+    """Between verify and refresh, NaN goes into the tree K/V and every scratch slot of the
+    nodes off the accepted path: the refreshed state is bit-identical to a clean run."""
+    import torch
+    _say("refresh isolation")
+    w = synth.Workload("iso", 4, 8, 16, 2, 128, "bf16", (4, 128), 126, 2, 3, 0.6, 3100, prefix="raw")
+    caps = pooled_caps(w, 64)
+    results = []
+    for poison in (False, True):
+        dst = device_state(w, caps)
+        r = Runner(dst, w.D, w.Hq)
+        for t in range(3):
+            s = synth.step_inputs(w, t)
+            x = upload_step(s, w.dtype)
+            r.plan(x)
+            r.attend(x)
+            r.accept(x)
+            if poison:
+                torch.cuda.synchronize()
+                m = r.m.cpu().numpy()
+                path = r.path.cpu().numpy()
+                for b in range(w.B):
+                    on = set(path[b, :m[b] + 1].tolist())
+                    off = [i for i in range(w.D) if i not in on]
+                    for t_ in (x.kt, x.vt):
+                        t_[b, off] = float("nan")
+                    for l in range(len(w.levels)):
+                        for t_ in (r.sc.entry_k[l], r.sc.entry_v[l], r.sc.open_k[l], r.sc.open_v[l]):
+                            t_[b, off] = float("nan")
+            r.refresh(x)
+        torch.cuda.synchronize()
+        results.append(dst)
+    a, b = results
+    assert torch.equal(a.P, b.P)
+    for l in range(len(w.levels)):
+        assert torch.equal(a.n[l], b.n[l])
+        assert torch.equal(a.pool_k[l].view(torch.int16), b.pool_k[l].view(torch.int16))
+        assert torch.equal(a.pool_vt[l].view(torch.int16), b.pool_vt[l].view(torch.int16))
+        assert torch.equal(a.open_k[l], b.open_k[l]) and torch.equal(a.open_v[l], b.open_v[l])
+    assert torch.equal(a.tail_k.view(torch.int16), b.tail_k.view(torch.int16))
+
+
+def test_pool_full_leaves_sequence_unchanged():
+    import torch
+    _say("refresh pool full")
+    w = synth.Workload("full", 3, 8, 8, 1, 64, "f32", (4,), 60, 1, 7, 1.0, 3200, prefix="raw")
+    # capacity 64 entries = 256 tokens; sequences start at 60 tokens (15 entries)
+    dst = device_state(w, [64])
+    dst.P.copy_(torch.tensor([60, 252, 255], dtype=torch.int32))
+    rk = np.stack([synth.raw_prefix(w, b, 255)[0] for b in range(w.B)])
+    import tree_speculative_decoding_amd as tv
+    err = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    tv.tv_compress_prefix(dst, tv.to_device(rk, "f32"), tv.to_device(rk, "f32"), err)
+    torch.cuda.synchronize()
+    before = [t.clone() for t in (dst.P, dst.n[0], dst.pool_k[0], dst.open_k[0], dst.tail_k)]
+    r = Runner(dst, w.D, w.Hq)
+    s = synth.step_inputs(w, 0)
+    x = upload_step(s, w.dtype)
+    r.step(x)
+    torch.cuda.synchronize()
+    m = r.m.cpu().numpy()
+    e = r.err.cpu().numpy()
+    P = dst.P.cpu().numpy()
+    assert (m == 7).all()  # p = 1: every draft accepted
+    assert e[0] == 0 and P[0] == 68
+    # 252 + 8 = 260 -> 65 entries > 64; 255 + 8 = 263 -> 65 entries
+    assert e[1] == tv.TV_SEQ_POOL_FULL and e[2] == tv.TV_SEQ_POOL_FULL
+    for b in (1, 2):
+        assert P[b] == before[0][b].item()
+        assert dst.n[0][b].item() == before[1][b].item()
+        assert torch.equal(dst.pool_k[0][b], before[2][b])
+        assert torch.equal(dst.open_k[0][b], before[3][b])
+        assert torch.equal(dst.tail_k[b], before[4][b])

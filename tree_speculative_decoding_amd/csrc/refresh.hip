@@ -1,0 +1,117 @@
+// Accepted-path refresh of the persistent compressed state.
+// TSD-V4 §3.2 (token history, cache and compressed states must describe one
+// prefix), §4.2 (only the accepted path's scratch states update the persistent
+// state; rejected branches are not carried over) and §4.3 (C4 / C128 states and
+// their compression-intermediate buffers).
+//
+// One workgroup per sequence.  Every committed element is a bit copy: scratch
+// entries of the path nodes that close a block go to the next pool slots, the
+// path leaf's open-block sums replace the open sums, path tokens extend the raw
+// tail.  Counters (P, n) are written after a barrier, once every thread of the
+// sequence has read the old values.  Rejected nodes are never read.
+#include "tv_common.h"
+
+namespace tv {
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_refresh(int D, tv_state st, tv_scratch sc,
+                                                 const T* __restrict__ k_tree,
+                                                 const T* __restrict__ v_tree,
+                                                 const int32_t* __restrict__ m_in,
+                                                 const int32_t* __restrict__ path,
+                                                 int32_t* __restrict__ commit_log,
+                                                 int32_t* __restrict__ seq_err) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int L = st.n_levels;
+  const int Hkv = st.Hkv, d = st.d, HD = Hkv * d;
+  if (commit_log != nullptr)
+    for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
+  const int err = seq_err[b];
+  const int m = m_in[b];
+  const int P = st.P[b];
+  __syncthreads();  // log prefill and the reads above happen before any later write
+  if (err != TV_SEQ_OK || m < 0) return;
+  const int32_t* pth = path + (size_t)b * D;
+  bool bad = m >= D || P < 0;
+  for (int t = 0; t <= m && !bad; ++t) bad = pth[t] < 0 || pth[t] >= D;
+  if (bad) {
+    if (tid == 0) seq_err[b] = TV_SEQ_BAD_PATH;
+    return;
+  }
+  const int P2 = P + m + 1;
+  bool full = false;
+  for (int l = 0; l < L; ++l) full |= (P2 / st.lvl[l].C) > st.lvl[l].cap;
+  if (full) {
+    if (tid == 0) seq_err[b] = TV_SEQ_POOL_FULL;
+    return;
+  }
+  const int leaf = pth[m];
+  for (int l = 0; l < L; ++l) {
+    const int C = st.lvl[l].C, cap = st.lvl[l].cap;
+    T* pk = (T*)st.lvl[l].k;
+    T* pvt = (T*)st.lvl[l].vt;
+    const T* ek = (const T*)sc.entry_k[l];
+    const T* ev = (const T*)sc.entry_v[l];
+    const int j0 = P / C, j1 = P2 / C;
+    for (int j = j0; j < j1; ++j) {
+      const int u = pth[j * C + C - 1 - P];  // path node at the block's last position
+      for (int e = tid; e < HD; e += nt) {
+        const int g = e / d, dd = e - g * d;
+        const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
+        pk[(((size_t)b * Hkv + g) * cap + j) * d + dd] = ek[src];
+        pvt[(((size_t)b * Hkv + g) * d + dd) * cap + j] = ev[src];
+      }
+      if (commit_log != nullptr && tid == 0) {
+        int32_t* row = commit_log + (((size_t)b * L + l) * D + (j - j0)) * 2;
+        row[0] = j;
+        row[1] = u;
+      }
+    }
+    const float* sok = sc.open_k[l] + ((size_t)b * D + leaf) * HD;
+    const float* sov = sc.open_v[l] + ((size_t)b * D + leaf) * HD;
+    for (int e = tid; e < HD; e += nt) {
+      st.lvl[l].open_k[(size_t)b * HD + e] = sok[e];
+      st.lvl[l].open_v[(size_t)b * HD + e] = sov[e];
+    }
+  }
+  if (L > 0 && st.lvl[0].C > 1) {
+    const int C0 = st.lvl[0].C;
+    const int t_new = (P2 / C0) * C0;
+    T* tk = (T*)st.tail_k;
+    T* tv_ = (T*)st.tail_v;
+    // positions below P keep their slot when no block closed (t_new == old start);
+    // when one closed, t_new > P and only path tokens remain
+    for (int pos = max(t_new, P); pos < P2; ++pos) {
+      const int u = pth[pos - P];
+      for (int e = tid; e < HD; e += nt) {
+        const int g = e / d, dd = e - g * d;
+        const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
+        const size_t dst = (((size_t)b * Hkv + g) * (C0 - 1) + (pos - t_new)) * d + dd;
+        tk[dst] = k_tree[src];
+        tv_[dst] = v_tree[src];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    st.P[b] = P2;
+    for (int l = 0; l < L; ++l) st.lvl[l].n[b] = P2 / st.lvl[l].C;
+  }
+}
+
+hipError_t launch_refresh(int D, const tv_state& st, const tv_scratch& sc, const void* k_tree,
+                          const void* v_tree, const int32_t* m, const int32_t* path,
+                          int32_t* commit_log, int32_t* seq_err, hipStream_t s) {
+  if (st.B == 0) return hipSuccess;
+  dim3 grid(st.B), block(256);
+  if (st.dtype == TV_BF16)
+    hipLaunchKernelGGL(k_refresh<uint16_t>, grid, block, 0, s, D, st, sc, (const uint16_t*)k_tree,
+                       (const uint16_t*)v_tree, m, path, commit_log, seq_err);
+  else
+    hipLaunchKernelGGL(k_refresh<float>, grid, block, 0, s, D, st, sc, (const float*)k_tree,
+                       (const float*)v_tree, m, path, commit_log, seq_err);
+  return hipGetLastError();
+}
+
+}  // namespace tv

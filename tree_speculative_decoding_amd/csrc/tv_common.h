@@ -1,0 +1,133 @@
+// Internal helpers shared by the HIP kernels of libtv (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tv.h"
+
+namespace tv {
+
+// ---------------------------------------------------------------- element types
+// bf16 values travel as raw 16-bit patterns; arithmetic is always fp32.
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even (gfx950 converts with v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+
+// ---------------------------------------------------------------- wave64 reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = (uint32_t)__shfl((int)lo, src, 64);
+  hi = (uint32_t)__shfl((int)hi, src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// bits of the nodes 0..D-1 of a tree
+__device__ __forceinline__ uint64_t node_mask(int D) { return D >= 64 ? ~0ull : ((1ull << D) - 1ull); }
+
+// committed entries of a level, never beyond the pool's capacity
+__device__ __forceinline__ int level_count(const int32_t* n, int b, int cap) {
+  return max(0, min(n[b], cap));
+}
+
+// log2(e): scores are kept in base-2 units (s * log2(e) / sqrt(d)) so exp2 can be used.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- launch arguments
+
+struct AttnArgs {
+  int B, D, Hq, Hkv, d, G, R;        // R = G * D query rows per (sequence, KV head)
+  int dtype;                         // tv_dtype
+  int n_levels;
+  int C[TV_MAX_LEVELS], cap[TV_MAX_LEVELS];
+  const void* pk[TV_MAX_LEVELS];     // pools, K row-major
+  const void* pvt[TV_MAX_LEVELS];    // pools, V transposed
+  const int32_t* pn[TV_MAX_LEVELS];
+  const float* open_k[TV_MAX_LEVELS];
+  const float* open_v[TV_MAX_LEVELS];
+  const void* tail_k;
+  const void* tail_v;
+  const int32_t* P;
+  const void* q;
+  const void* k_tree;
+  const void* v_tree;
+  const uint64_t* anc;
+  const int32_t* depth;
+  const int32_t* seq_err;            // may be null
+  void* out;
+  float* lse;                        // may be null
+  tv_scratch scratch;                // entries may be null
+  int build_scratch;
+  int splits;                        // split-KV partitions per (sequence, KV head, row block)
+  int row_blocks;                    // ceil(R / 64)
+  int tiles_cap;                     // upper bound of 64-entry tiles over all levels
+  float* ws_o;                       // [B][Hkv][splits][R][d]
+  float2* ws_ml;                     // [B][Hkv][splits][R] (running max in log2 units, sum)
+  float scale_log2;                  // log2(e) / sqrt(d)
+};
+
+// The prefix of a (sequence, KV head) is streamed as 64-entry chunks: level 0's
+// ceil(n0/64) chunks, then level 1's.  Splits take equal runs of chunks, so a
+// chunk never straddles two levels and always starts 64-aligned in its pool.
+// chunk c of a sequence's concatenated pools -> (level, first entry, entry count)
+__device__ __forceinline__ void chunk_entries(int n0, int T0, int n1, int c, int* lvl,
+                                              int* e0, int* cnt) {
+  if (c < T0) {
+    *lvl = 0;
+    *e0 = c * 64;
+    *cnt = min(64, n0 - c * 64);
+  } else {
+    *lvl = 1;
+    *e0 = (c - T0) * 64;
+    *cnt = min(64, n1 - (c - T0) * 64);
+  }
+}
+
+hipError_t launch_tree_mask(int B, int D, const int32_t* parents, uint64_t* anc, int32_t* depth,
+                            int32_t* seq_err, hipStream_t s);
+hipError_t launch_accept(int B, int D, const int32_t* parents, const uint64_t* anc,
+                         const int32_t* depth, const int32_t* draft, const int32_t* target,
+                         const int32_t* seq_err, int32_t* m, int32_t* path, int32_t* bonus,
+                         hipStream_t s);
+hipError_t launch_refresh(int D, const tv_state& st, const tv_scratch& sc, const void* k_tree,
+                          const void* v_tree, const int32_t* m, const int32_t* path,
+                          int32_t* commit_log, int32_t* seq_err, hipStream_t s);
+hipError_t launch_compress(const tv_state& st, const void* raw_k, const void* raw_v, int max_len,
+                           int32_t* seq_err, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_scratch(const AttnArgs& a, hipStream_t s);
+
+}  // namespace tv

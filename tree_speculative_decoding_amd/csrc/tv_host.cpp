@@ -1,0 +1,254 @@
+// libtv host entry points: argument validation, split-KV planning and kernel
+// launches.  Nothing here allocates device memory or synchronises; every check
+// that can be made on the host happens before the first launch of a call.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "tv.h"
+#include "tv_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+tv_status fail(tv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tv_status ok() {
+  g_err[0] = '\0';
+  return TV_OK;
+}
+
+tv_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TV_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape and pointer checks of a state; `need_tail` only matters when a level exists.
+tv_status check_state(const tv_state* st) {
+  if (st == nullptr) return fail(TV_EINVAL, "state is NULL");
+  if (st->B < 0) return fail(TV_EINVAL, "B = %d < 0", st->B);
+  if (st->Hkv < 1) return fail(TV_EINVAL, "Hkv = %d < 1", st->Hkv);
+  if (st->d != 64 && st->d != 128) return fail(TV_EUNSUPPORTED, "head dim %d (supported: 64, 128)", st->d);
+  if (st->dtype != TV_F32 && st->dtype != TV_BF16) return fail(TV_EINVAL, "dtype %d", st->dtype);
+  if (st->n_levels < 0 || st->n_levels > TV_MAX_LEVELS)
+    return fail(TV_EINVAL, "n_levels = %d (0..%d)", st->n_levels, TV_MAX_LEVELS);
+  if (st->P == nullptr) return fail(TV_EINVAL, "state P is NULL");
+  for (int l = 0; l < st->n_levels; ++l) {
+    const tv_level& L = st->lvl[l];
+    if (L.C < 1) return fail(TV_EINVAL, "level %d: C = %d < 1", l, L.C);
+    if (l > 0 && L.C <= st->lvl[l - 1].C) return fail(TV_EINVAL, "level block sizes must increase");
+    if (L.cap < 0 || L.cap % TV_POOL_ALIGN != 0)
+      return fail(TV_EINVAL, "level %d: cap = %d must be a non-negative multiple of %d", l, L.cap,
+                  TV_POOL_ALIGN);
+    if (!L.k || !L.vt || !L.n || !L.open_k || !L.open_v)
+      return fail(TV_EINVAL, "level %d: NULL pool/count/open-sum pointer", l);
+    if (!aligned16(L.k) || !aligned16(L.vt)) return fail(TV_EINVAL, "level %d: pools must be 16-byte aligned", l);
+  }
+  if (st->n_levels > 0 && st->lvl[0].C > 1 && (!st->tail_k || !st->tail_v))
+    return fail(TV_EINVAL, "tail pointers are NULL");
+  return ok();
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+struct Plan {
+  int R, row_blocks, tiles_cap, splits;
+  size_t ws_o_bytes, ws_ml_off, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Split-KV plan.  Every (sequence, KV head, 64-row block) is a unit; auto mode
+// gives each unit enough splits to put ~4 workgroups on every compute unit, but
+// keeps >= 16 chunks (1024 entries) per split so the partials stay a few percent
+// of the streamed bytes.
+Plan make_plan(int D, int Hq, const tv_state* st, int num_splits) {
+  Plan p{};
+  const int G = Hq / st->Hkv;
+  p.R = G * D;
+  p.row_blocks = (p.R + 63) / 64;
+  p.tiles_cap = 0;
+  for (int l = 0; l < st->n_levels; ++l) p.tiles_cap += (st->lvl[l].cap + 63) / 64;
+  if (num_splits > 0) {
+    p.splits = num_splits;
+  } else {
+    const long units = (long)st->B * st->Hkv * p.row_blocks;
+    const long target = 4L * device_cus();
+    long s = units > 0 ? (target + units - 1) / units : 1;
+    const long max_s = p.tiles_cap / 16 > 1 ? p.tiles_cap / 16 : 1;
+    if (s > max_s) s = max_s;
+    if (s < 1) s = 1;
+    p.splits = (int)s;
+  }
+  const size_t rows = (size_t)st->B * st->Hkv * p.splits * p.R;
+  p.ws_o_bytes = round256(rows * st->d * sizeof(float));
+  p.ws_ml_off = p.ws_o_bytes;
+  p.total = p.ws_o_bytes + round256(rows * sizeof(float2));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+TV_API const char* tv_status_string(tv_status s) {
+  switch (s) {
+    case TV_OK: return "ok";
+    case TV_EINVAL: return "invalid argument";
+    case TV_EUNSUPPORTED: return "unsupported configuration";
+    case TV_EWORKSPACE: return "workspace too small";
+    case TV_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+TV_API const char* tv_last_error(void) { return g_err; }
+
+TV_API int tv_version(void) { return TV_VERSION; }
+
+TV_API tv_status tv_set_timing_events(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return fail(TV_EINVAL, "give both events or neither");
+  g_ev_start = start;
+  g_ev_stop = stop;
+  return ok();
+}
+
+TV_API tv_status tv_build_tree_mask(int B, int D, const int32_t* parents, uint64_t* anc, int32_t* depth,
+                                    int32_t* seq_err, hipStream_t stream) {
+  if (B < 0) return fail(TV_EINVAL, "B = %d < 0", B);
+  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
+  if (B == 0) return ok();
+  if (!parents || !anc || !depth || !seq_err) return fail(TV_EINVAL, "NULL pointer argument");
+  return hip_check(tv::launch_tree_mask(B, D, parents, anc, depth, seq_err, stream), "tree mask launch");
+}
+
+TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_splits) {
+  if (D < 1 || D > TV_MAX_D || Hq < 1 || num_splits < 0) return 0;
+  if (check_state(st) != TV_OK) return 0;
+  if (Hq % st->Hkv != 0) return 0;
+  return make_plan(D, Hq, st, num_splits).total;
+}
+
+TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree, const void* v_tree,
+                                const uint64_t* anc, const int32_t* depth, const int32_t* seq_err,
+                                const tv_state* st, const tv_scratch* scratch, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, int num_splits,
+                                hipStream_t stream) {
+  tv_status s = check_state(st);
+  if (s != TV_OK) return s;
+  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
+  if (Hq < 1 || Hq % st->Hkv != 0) return fail(TV_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, st->Hkv);
+  if (num_splits < 0) return fail(TV_EINVAL, "num_splits = %d < 0", num_splits);
+  if (st->B == 0) return ok();
+  if (!q || !k_tree || !v_tree || !anc || !depth || !out) return fail(TV_EINVAL, "NULL pointer argument");
+  if (!aligned16(q)) return fail(TV_EINVAL, "q must be 16-byte aligned");
+  if (scratch != nullptr)
+    for (int l = 0; l < st->n_levels; ++l)
+      if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
+        return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
+  const Plan p = make_plan(D, Hq, st, num_splits);
+  if (workspace == nullptr || workspace_bytes < p.total)
+    return fail(TV_EWORKSPACE, "workspace %zu bytes, need %zu", workspace == nullptr ? (size_t)0 : workspace_bytes,
+                p.total);
+  if (!aligned16(workspace)) return fail(TV_EINVAL, "workspace must be 16-byte aligned");
+
+  tv::AttnArgs a{};
+  a.B = st->B; a.D = D; a.Hq = Hq; a.Hkv = st->Hkv; a.d = st->d; a.G = Hq / st->Hkv; a.R = p.R;
+  a.dtype = st->dtype; a.n_levels = st->n_levels;
+  for (int l = 0; l < st->n_levels; ++l) {
+    a.C[l] = st->lvl[l].C; a.cap[l] = st->lvl[l].cap;
+    a.pk[l] = st->lvl[l].k; a.pvt[l] = st->lvl[l].vt; a.pn[l] = st->lvl[l].n;
+    a.open_k[l] = st->lvl[l].open_k; a.open_v[l] = st->lvl[l].open_v;
+  }
+  a.tail_k = st->tail_k; a.tail_v = st->tail_v; a.P = st->P;
+  a.q = q; a.k_tree = k_tree; a.v_tree = v_tree; a.anc = anc; a.depth = depth; a.seq_err = seq_err;
+  a.out = out; a.lse = lse;
+  if (scratch != nullptr) a.scratch = *scratch;
+  a.build_scratch = scratch != nullptr;
+  a.splits = p.splits; a.row_blocks = p.row_blocks; a.tiles_cap = p.tiles_cap;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
+  a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);
+
+  const bool mfma = st->dtype == TV_BF16 && st->d == 128;
+  if (g_ev_start) {
+    s = hip_check(hipEventRecord(g_ev_start, stream), "timing event");
+    if (s != TV_OK) return s;
+  }
+  s = hip_check(mfma ? tv::launch_attn_mfma(a, stream) : tv::launch_attn_valu(a, stream), "prefix attention launch");
+  if (s != TV_OK) return s;
+  if (g_ev_stop) {
+    s = hip_check(hipEventRecord(g_ev_stop, stream), "timing event");
+    if (s != TV_OK) return s;
+  }
+  s = hip_check(tv::launch_attn_merge(a, stream), "attention merge launch");
+  if (s != TV_OK) return s;
+  if (a.build_scratch) s = hip_check(tv::launch_scratch(a, stream), "scratch launch");
+  return s;
+}
+
+TV_API tv_status tv_accept(int B, int D, const int32_t* parents, const uint64_t* anc, const int32_t* depth,
+                           const int32_t* draft_tok, const int32_t* target_tok, const int32_t* seq_err,
+                           int32_t* m, int32_t* path, int32_t* bonus, hipStream_t stream) {
+  if (B < 0) return fail(TV_EINVAL, "B = %d < 0", B);
+  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
+  if (B == 0) return ok();
+  if (!parents || !anc || !depth || !draft_tok || !target_tok || !m || !path || !bonus)
+    return fail(TV_EINVAL, "NULL pointer argument");
+  return hip_check(tv::launch_accept(B, D, parents, anc, depth, draft_tok, target_tok, seq_err, m, path, bonus,
+                                     stream),
+                   "accept launch");
+}
+
+TV_API tv_status tv_refresh_state(int D, const tv_state* st, const tv_scratch* scratch, const void* k_tree,
+                                  const void* v_tree, const int32_t* m, const int32_t* path,
+                                  int32_t* commit_log, int32_t* seq_err, hipStream_t stream) {
+  tv_status s = check_state(st);
+  if (s != TV_OK) return s;
+  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
+  if (st->B == 0) return ok();
+  if (!k_tree || !v_tree || !m || !path || !seq_err) return fail(TV_EINVAL, "NULL pointer argument");
+  tv_scratch sc{};
+  if (st->n_levels > 0) {
+    if (scratch == nullptr) return fail(TV_EINVAL, "scratch is NULL");
+    for (int l = 0; l < st->n_levels; ++l)
+      if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
+        return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
+    sc = *scratch;
+  }
+  return hip_check(tv::launch_refresh(D, *st, sc, k_tree, v_tree, m, path, commit_log, seq_err, stream),
+                   "refresh launch");
+}
+
+TV_API tv_status tv_compress_prefix(const tv_state* st, const void* raw_k, const void* raw_v, int max_len,
+                                    int32_t* seq_err, hipStream_t stream) {
+  tv_status s = check_state(st);
+  if (s != TV_OK) return s;
+  if (max_len < 0) return fail(TV_EINVAL, "max_len = %d < 0", max_len);
+  if (st->B == 0) return ok();
+  if (!seq_err) return fail(TV_EINVAL, "NULL seq_err");
+  if (max_len > 0 && (!raw_k || !raw_v)) return fail(TV_EINVAL, "NULL raw prefix pointer");
+  return hip_check(tv::launch_compress(*st, raw_k, raw_v, max_len, seq_err, stream), "compress launch");
+}
+
+}  // extern "C"

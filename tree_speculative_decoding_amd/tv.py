@@ -1,0 +1,264 @@
+"""ctypes binding of libtv (include/tv.h): the same entry points, taking torch tensors.
+
+This module only marshals arguments: it turns tensors into device pointers, fills
+the tv_state / tv_scratch structs and raises on a non-OK status.  Every step of
+the path runs in the HIP kernels of libtv.so; there is no fallback.  PyTorch is
+used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtv.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "tv.h")
+
+TV_OK, TV_EINVAL, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = 0, -1, -2, -3, -4
+TV_F32, TV_BF16 = 0, 1
+TV_SEQ_OK, TV_SEQ_BAD_PARENT, TV_SEQ_POOL_FULL, TV_SEQ_BAD_PREFIX, TV_SEQ_BAD_PATH = 0, 1, 2, 3, 4
+TV_MAX_LEVELS = 2
+TV_MAX_D = 64
+TV_POOL_ALIGN = 64
+
+
+class TvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"tv status {status}: {msg}")
+        self.status = status
+
+
+class TvLevel(ctypes.Structure):
+    _fields_ = [("C", ctypes.c_int32), ("cap", ctypes.c_int32), ("k", ctypes.c_void_p),
+                ("vt", ctypes.c_void_p), ("n", ctypes.c_void_p), ("open_k", ctypes.c_void_p),
+                ("open_v", ctypes.c_void_p)]
+
+
+class TvState(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("n_levels", ctypes.c_int32),
+                ("lvl", TvLevel * TV_MAX_LEVELS), ("tail_k", ctypes.c_void_p),
+                ("tail_v", ctypes.c_void_p), ("P", ctypes.c_void_p)]
+
+
+class TvScratch(ctypes.Structure):
+    _fields_ = [("entry_k", ctypes.c_void_p * TV_MAX_LEVELS), ("entry_v", ctypes.c_void_p * TV_MAX_LEVELS),
+                ("open_k", ctypes.c_void_p * TV_MAX_LEVELS), ("open_v", ctypes.c_void_p * TV_MAX_LEVELS)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtv.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m tree_speculative_decoding_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        sig = {
+            "tv_build_tree_mask": ([i32, i32, vp, vp, vp, vp, vp], i32),
+            "tv_verify_attn_workspace_bytes": ([i32, i32, ctypes.POINTER(TvState), i32], sz),
+            "tv_verify_attn": ([i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TvState),
+                                ctypes.POINTER(TvScratch), vp, vp, vp, sz, i32, vp], i32),
+            "tv_accept": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+            "tv_refresh_state": ([i32, ctypes.POINTER(TvState), ctypes.POINTER(TvScratch), vp, vp, vp,
+                                  vp, vp, vp, vp], i32),
+            "tv_compress_prefix": ([ctypes.POINTER(TvState), vp, vp, i32, vp, vp], i32),
+            "tv_set_timing_events": ([vp, vp], i32),
+            "tv_status_string": ([i32], ctypes.c_char_p),
+            "tv_last_error": ([], ctypes.c_char_p),
+            "tv_version": ([], i32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/tv.h declares."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"TV_API\s+[^;(]*?\b(tv_\w+)\s*\(", txt)))
+
+
+# ----------------------------------------------------------------------------- marshalling
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libtv must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(status: int):
+    if status != TV_OK:
+        raise TvError(status, lib().tv_last_error().decode())
+
+
+def torch_dtype(dtype: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+
+def tv_dtype(dtype: str) -> int:
+    return {"bf16": TV_BF16, "f32": TV_F32}[dtype]
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """numpy input (bf16 as uint16 bit patterns, or float32) -> device tensor of that dtype."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy (bf16 as uint16 bit patterns)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def round_cap(n: int) -> int:
+    return max(TV_POOL_ALIGN, -(-n // TV_POOL_ALIGN) * TV_POOL_ALIGN)
+
+
+class DeviceState:
+    """Device tensors of a tv_state: pools (K row-major, V transposed), counts, open
+    sums, tail and committed lengths.  Allocation only; no arithmetic."""
+
+    def __init__(self, B: int, Hkv: int, d: int, dtype: str, levels: Sequence[int],
+                 caps: Sequence[int], device="cuda"):
+        if len(levels) > TV_MAX_LEVELS:
+            raise ValueError("at most two levels")
+        self.B, self.Hkv, self.d, self.dtype = B, Hkv, d, dtype
+        self.levels = tuple(int(c) for c in levels)
+        self.caps = tuple(round_cap(int(c)) for c in caps)
+        td = torch_dtype(dtype)
+        z = lambda *s, dt=td: torch.zeros(*s, dtype=dt, device=device)
+        self.pool_k = [z(B, Hkv, c, d) for c in self.caps]
+        self.pool_vt = [z(B, Hkv, d, c) for c in self.caps]
+        self.n = [z(B, dt=torch.int32) for _ in self.levels]
+        self.open_k = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
+        self.open_v = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
+        c0 = self.levels[0] if self.levels else 1
+        self.tail_k = z(B, Hkv, c0 - 1, d) if c0 > 1 else None
+        self.tail_v = z(B, Hkv, c0 - 1, d) if c0 > 1 else None
+        self.P = z(B, dt=torch.int32)
+
+    def struct(self) -> TvState:
+        s = TvState()
+        s.B, s.Hkv, s.d, s.dtype, s.n_levels = self.B, self.Hkv, self.d, tv_dtype(self.dtype), len(self.levels)
+        for l, C in enumerate(self.levels):
+            L = s.lvl[l]
+            L.C, L.cap = C, self.caps[l]
+            L.k, L.vt = self.pool_k[l].data_ptr(), self.pool_vt[l].data_ptr()
+            L.n = self.n[l].data_ptr()
+            L.open_k, L.open_v = self.open_k[l].data_ptr(), self.open_v[l].data_ptr()
+        s.tail_k = self.tail_k.data_ptr() if self.tail_k is not None else None
+        s.tail_v = self.tail_v.data_ptr() if self.tail_v is not None else None
+        s.P = self.P.data_ptr()
+        return s
+
+
+class DeviceScratch:
+    """Device tensors of a tv_scratch for B sequences of D nodes."""
+
+    def __init__(self, B: int, D: int, Hkv: int, d: int, dtype: str, n_levels: int, device="cuda"):
+        td = torch_dtype(dtype)
+        self.entry_k = [torch.zeros(B, D, Hkv, d, dtype=td, device=device) for _ in range(n_levels)]
+        self.entry_v = [torch.zeros(B, D, Hkv, d, dtype=td, device=device) for _ in range(n_levels)]
+        self.open_k = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
+        self.open_v = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
+
+    def struct(self) -> TvScratch:
+        s = TvScratch()
+        for l in range(len(self.entry_k)):
+            s.entry_k[l] = self.entry_k[l].data_ptr()
+            s.entry_v[l] = self.entry_v[l].data_ptr()
+            s.open_k[l] = self.open_k[l].data_ptr()
+            s.open_v[l] = self.open_v[l].data_ptr()
+        return s
+
+
+def _state(st) -> TvState:
+    return st.struct() if isinstance(st, DeviceState) else st
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def tv_build_tree_mask(parents: torch.Tensor, anc: torch.Tensor, depth: torch.Tensor,
+                       seq_err: torch.Tensor, stream=None) -> None:
+    B, D = parents.shape
+    _check(lib().tv_build_tree_mask(B, D, _ptr(parents), _ptr(anc), _ptr(depth), _ptr(seq_err),
+                                    _stream(stream)))
+
+
+def tv_verify_attn_workspace_bytes(D: int, Hq: int, st, num_splits: int = 0) -> int:
+    s = _state(st)
+    return int(lib().tv_verify_attn_workspace_bytes(D, Hq, ctypes.byref(s), num_splits))
+
+
+def tv_verify_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, anc: torch.Tensor,
+                   depth: torch.Tensor, seq_err: Optional[torch.Tensor], st, scratch,
+                   out: torch.Tensor, lse: Optional[torch.Tensor], workspace: torch.Tensor,
+                   num_splits: int = 0, stream=None) -> None:
+    B, D, Hq, d = q.shape
+    s = _state(st)
+    sc = scratch.struct() if isinstance(scratch, DeviceScratch) else scratch
+    _check(lib().tv_verify_attn(D, Hq, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(anc), _ptr(depth),
+                                _ptr(seq_err), ctypes.byref(s),
+                                ctypes.byref(sc) if sc is not None else None, _ptr(out), _ptr(lse),
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                num_splits, _stream(stream)))
+
+
+def tv_accept(parents, anc, depth, draft_tok, target_tok, seq_err, m, path, bonus, stream=None) -> None:
+    B, D = parents.shape
+    _check(lib().tv_accept(B, D, _ptr(parents), _ptr(anc), _ptr(depth), _ptr(draft_tok), _ptr(target_tok),
+                           _ptr(seq_err), _ptr(m), _ptr(path), _ptr(bonus), _stream(stream)))
+
+
+def tv_refresh_state(st, scratch, k_tree, v_tree, m, path, commit_log, seq_err, stream=None) -> None:
+    D = k_tree.shape[1]
+    s = _state(st)
+    sc = scratch.struct() if isinstance(scratch, DeviceScratch) else scratch
+    _check(lib().tv_refresh_state(D, ctypes.byref(s), ctypes.byref(sc) if sc is not None else None,
+                                  _ptr(k_tree), _ptr(v_tree), _ptr(m), _ptr(path), _ptr(commit_log),
+                                  _ptr(seq_err), _stream(stream)))
+
+
+def tv_compress_prefix(st, raw_k: torch.Tensor, raw_v: torch.Tensor, seq_err: torch.Tensor,
+                       stream=None) -> None:
+    s = _state(st)
+    max_len = raw_k.shape[2]
+    _check(lib().tv_compress_prefix(ctypes.byref(s), _ptr(raw_k), _ptr(raw_v), max_len, _ptr(seq_err),
+                                    _stream(stream)))
+
+
+def tv_set_timing_events(start, stop) -> None:
+    a = ctypes.c_void_p(start.cuda_event) if start is not None else None
+    b = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
+    _check(lib().tv_set_timing_events(a, b))
+
+
+def tv_version() -> int:
+    return int(lib().tv_version())
