@@ -42,8 +42,23 @@ def parse():
     ap.add_argument("--workload", default="high_batch")
     ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (to scale HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """Plain copies of a known size: what FETCH_SIZE / WRITE_SIZE read for them gives the
+    counters' scale (bytes counted per byte moved)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
 
 
 def kernel_source_digest() -> str:
@@ -73,6 +88,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU "
               "in this build.", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import torch
 

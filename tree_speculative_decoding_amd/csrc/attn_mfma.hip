@@ -9,7 +9,7 @@
 // rows per wave (rows r = node * G + head-in-group).  Per 64-entry chunk:
 //   1. the K chunk (64 x 128, row-major) and the transposed V chunk (128 x 64)
 //      are loaded with 16-byte coalesced loads into registers one chunk ahead,
-//      then written to LDS (straight copies, padded rows);
+//      all issued back to back, then written to LDS (straight copies, padded rows);
 //   2. S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the K chunk is the A operand
 //      (16 entries x 32 channels per lane group), Q^T the B operand kept in
 //      registers for the whole kernel; the accumulator gives each lane one query
@@ -36,13 +36,14 @@ constexpr int kChunk = 64;      // entries per chunk
 constexpr int kKStr = kDH * 2 + 16;      // LDS bytes per K row (padded)
 constexpr int kVStr = kChunk * 2 + 16;   // LDS bytes per V^T row (padded)
 constexpr int kLdsBytes = kChunk * kKStr + kDH * kVStr;
-constexpr int kPieces = 2 * kChunk * kDH * 2 / 16;  // 16-byte pieces per chunk (K + V^T)
 }  // namespace
 
+// At most 168 VGPRs, so three workgroups fit on a CU (LDS allows four).
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 3) void k_attn_mfma(AttnArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int PER = (kPieces + NT - 1) / NT;
+  constexpr int PER = (1024 + NT - 1) / NT;   // K pieces (and V pieces) per thread
+  constexpr bool kFull = 1024 % NT == 0;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
   char* Ks = smem;
   char* Vs = smem + kChunk * kKStr;
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
 
   // Q^T operand: lane (n16, grp), k-step ks holds Q[row][32ks + 8grp .. +7]
   const int row = rb * 64 + w * 16 + n16;
+  const bool wave_has_rows = rb * 64 + w * 16 < a.R;  // wave-uniform
   bf16x8 qop[4];
   {
     const uint16_t* q = (const uint16_t*)a.q;
@@ -80,53 +82,44 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
   const int c_lo = s * per;
   const int c_hi = live ? min(T0 + T1, c_lo + per) : c_lo;
 
-  uint4 pre[PER];
-  // piece p < 1024: K row p/16, 16-byte column p%16; p >= 1024: V^T row (p-1024)/8, column %8
+  // Pieces: 1024 16-byte pieces of K (row p/16, column p%16) and 1024 of V^T (row p/8,
+  // column p%8) per chunk; thread tid takes pieces tid, tid + NT, ...  A chunk is
+  // 64-aligned in its pool and a pool's capacity is a multiple of 64, so all 64 entries of
+  // a chunk are in bounds: every piece is loaded unconditionally (no data-dependent code
+  // between the loads, so they are all in flight together) and entries past the committed
+  // count are zeroed by selection when the chunk is written to LDS.
+  uint4 kpre[PER], vpre[PER];
   auto load_chunk = [&](int c) {
     int lvl, e0, cnt;
     chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
-    const char* pk = (const char*)a.pk[lvl];
-    const char* pv = (const char*)a.pvt[lvl];
-    const size_t cap = (size_t)a.cap[lvl];
+    const uint32_t cap = (uint32_t)a.cap[lvl];
+    const char* kb = (const char*)a.pk[lvl] + (bg * cap + e0) * (kDH * 2);   // uniform
+    const char* vb = (const char*)a.pvt[lvl] + (bg * kDH * cap + e0) * 2;    // uniform
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       const int p = tid + x * NT;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (p < 1024) {
-        const int r = p >> 4, col = p & 15;
-        if (r < cnt) v = *(const uint4*)(pk + ((bg * cap + e0 + r) * kDH + col * 8) * 2);
-      } else if (p < kPieces) {
-        const int q = p - 1024;
-        const int dr = q >> 3, col = q & 7;
-        const int e_first = col * 8;
-        if (e_first < cnt) {
-          v = *(const uint4*)(pv + ((bg * kDH + dr) * cap + e0 + e_first) * 2);
-          const int keep = cnt - e_first;  // entries of this piece that are committed
-          if (keep < 8) {
-            // zero uncommitted entries (select, never arithmetic: they may hold anything)
-            uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const uint32_t lo_ok = (2 * h) < keep ? 0x0000ffffu : 0u;
-              const uint32_t hi_ok = (2 * h + 1) < keep ? 0xffff0000u : 0u;
-              w4[h] &= (lo_ok | hi_ok);
-            }
-            v = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-          }
-        }
+      if (kFull || p < 1024) {
+        kpre[x] = *(const uint4*)(kb + (uint32_t)p * 16);  // K rows are 256 B: piece p at 16p
+        vpre[x] = *(const uint4*)(vb + ((uint32_t)(p >> 3) * cap + (uint32_t)(p & 7) * 8) * 2);
       }
-      pre[x] = v;
     }
   };
-  auto store_chunk = [&]() {
+  auto store_chunk = [&](int cnt) {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       const int p = tid + x * NT;
-      if (p < 1024) {
-        *(uint4*)(Ks + (p >> 4) * kKStr + (p & 15) * 16) = pre[x];
-      } else if (p < kPieces) {
-        const int q = p - 1024;
-        *(uint4*)(Vs + (q >> 3) * kVStr + (q & 7) * 16) = pre[x];
+      if (kFull || p < 1024) {
+        const uint32_t krow_ok = (p >> 4) < cnt ? 0xffffffffu : 0u;
+        uint4 kv = kpre[x];
+        kv.x &= krow_ok; kv.y &= krow_ok; kv.z &= krow_ok; kv.w &= krow_ok;
+        *(uint4*)(Ks + (p >> 4) * kKStr + (p & 15) * 16) = kv;
+        const int keep = cnt - (p & 7) * 8;  // committed entries among this piece's 8
+        uint4 vv = vpre[x];
+        vv.x &= (keep > 0 ? 0x0000ffffu : 0u) | (keep > 1 ? 0xffff0000u : 0u);
+        vv.y &= (keep > 2 ? 0x0000ffffu : 0u) | (keep > 3 ? 0xffff0000u : 0u);
+        vv.z &= (keep > 4 ? 0x0000ffffu : 0u) | (keep > 5 ? 0xffff0000u : 0u);
+        vv.w &= (keep > 6 ? 0x0000ffffu : 0u) | (keep > 7 ? 0xffff0000u : 0u);
+        *(uint4*)(Vs + (p >> 3) * kVStr + (p & 7) * 16) = vv;
       }
     }
   };
@@ -141,9 +134,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
     int lvl, e0, cnt;
     chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
     __syncthreads();  // every wave is done reading the previous chunk
-    store_chunk();
+    store_chunk(cnt);
     __syncthreads();
     if (c + 1 < c_hi) load_chunk(c + 1);  // in flight while this chunk is computed
+    if (!wave_has_rows) continue;
 
     // S^T tiles: sacc[t] lane (n16, grp) = S[row n16][entry 16t + 4grp + i]
     f32x4 sacc[4];
@@ -212,16 +206,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a) {
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-  // waves per workgroup: enough 16-row tiles for the rows of one 64-row block
-  const int rows = a.row_blocks > 1 ? 64 : a.R;
-  const int nw = (rows + 15) / 16;
+  // Always four waves: all of them load (32 KB per chunk), waves whose 16 rows are all
+  // past the G*D query rows skip the arithmetic.
   dim3 grid(a.splits, a.Hkv * a.row_blocks, a.B);
-  switch (nw) {
-    case 1: hipLaunchKernelGGL(k_attn_mfma<1>, grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(k_attn_mfma<2>, grid, dim3(128), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(k_attn_mfma<3>, grid, dim3(192), 0, s, a); break;
-    default: hipLaunchKernelGGL(k_attn_mfma<4>, grid, dim3(256), 0, s, a); break;
-  }
+  hipLaunchKernelGGL(k_attn_mfma<4>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -78,10 +78,11 @@ struct Plan {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Split-KV plan.  Every (sequence, KV head, 64-row block) is a unit; auto mode
-// gives each unit enough splits to put ~4 workgroups on every compute unit, but
-// keeps >= 16 chunks (1024 entries) per split so the partials stay a few percent
-// of the streamed bytes.
+// Split-KV plan.  Every (sequence, KV head, 64-row block) is a unit whose prefix is
+// streamed by `splits` workgroups.  Auto mode picks the split count that minimises the
+// modelled time: the workgroups run in ceil(units*splits / slots) rounds of equal
+// length (slots = CUs x resident workgroups per CU), and every split adds its partial
+// rows (written once, read once by the merge) to the bytes each unit streams.
 Plan make_plan(int D, int Hq, const tv_state* st, int num_splits) {
   Plan p{};
   const int G = Hq / st->Hkv;
@@ -92,13 +93,23 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_splits) {
   if (num_splits > 0) {
     p.splits = num_splits;
   } else {
-    const long units = (long)st->B * st->Hkv * p.row_blocks;
-    const long target = 4L * device_cus();
-    long s = units > 0 ? (target + units - 1) / units : 1;
-    const long max_s = p.tiles_cap / 16 > 1 ? p.tiles_cap / 16 : 1;
-    if (s > max_s) s = max_s;
-    if (s < 1) s = 1;
-    p.splits = (int)s;
+    const bool mfma = st->dtype == TV_BF16 && st->d == 128;
+    const double slots = (double)device_cus() * (mfma ? 3 : 1);
+    const double units = (double)st->B * st->Hkv * p.row_blocks;
+    const double esz = st->dtype == TV_BF16 ? 2.0 : 4.0;
+    const double unit_bytes = (double)p.tiles_cap * 64 * st->d * 2 * esz + 1.0;
+    const double partial_bytes = 2.0 * 64 * (st->d + 2) * 4;  // one split's rows, written + read
+    const int max_s = p.tiles_cap / 8 > 1 ? p.tiles_cap / 8 : 1;  // >= 8 chunks per split
+    double best = 1e300;
+    p.splits = 1;
+    for (int s = 1; s <= max_s && s <= 256; ++s) {
+      const double rounds = std::ceil(units * s / slots);
+      const double cost = rounds * (unit_bytes / s + partial_bytes);
+      if (cost < best * 0.999) {
+        best = cost;
+        p.splits = s;
+      }
+    }
   }
   const size_t rows = (size_t)st->B * st->Hkv * p.splits * p.R;
   p.ws_o_bytes = round256(rows * st->d * sizeof(float));
