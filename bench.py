@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="high_batch")
-    ap.add_argument("--splits", type=int, default=0, help="split-KV partitions (0 = library's choice)")
+    ap.add_argument("--parts", type=int, default=0, help="prefix-stream workgroups (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -112,14 +112,14 @@ def main():
     import concurrent.futures as cf
 
     def draw(b):
-        return [(k, np.ascontiguousarray(v.transpose(0, 2, 1))) for k, v in synth.pooled_prefix(w, b)]
+        return [(k, tv.tv.tile_vt(v, st.caps[l])) for l, (k, v) in enumerate(synth.pooled_prefix(w, b))]
 
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
         for b, lv in enumerate(ex.map(draw, range(B))):
             for l, (k, vt) in enumerate(lv):
                 n = k.shape[1]
                 st.pool_k[l][b, :, :n] = tv.to_device(k, w.dtype)
-                st.pool_vt[l][b, :, :, :n] = tv.to_device(vt, w.dtype)
+                st.pool_vt[l][b] = tv.to_device(vt, w.dtype)
                 st.n[l][b] = n
     st.P.fill_(w.P)
 
@@ -141,7 +141,7 @@ def main():
     bonus = torch.zeros(B, dtype=torch.int32, device=dev)
     log = torch.zeros(B, len(w.levels), D, 2, dtype=torch.int32, device=dev)
     sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels))
-    ws_bytes = tv.tv_verify_attn_workspace_bytes(D, Hq, st, args.splits)
+    ws_bytes = tv.tv_verify_attn_workspace_bytes(D, Hq, st, args.parts)
     ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -149,7 +149,7 @@ def main():
 
     def one_step(x):
         tv.tv_build_tree_mask(x["parents"], anc, depth, err, stream)
-        tv.tv_verify_attn(x["q"], x["kt"], x["vt"], anc, depth, err, st, sc, out, lse, ws, args.splits, stream)
+        tv.tv_verify_attn(x["q"], x["kt"], x["vt"], anc, depth, err, st, sc, out, lse, ws, args.parts, stream)
         tv.tv_accept(x["parents"], anc, depth, x["draft"], x["target"], err, m, path, bonus, stream)
         tv.tv_refresh_state(st, sc, x["kt"], x["vt"], m, path, log, err, stream)
 
@@ -203,7 +203,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "D": D, "Hq": Hq, "Hkv": Hkv, "head_dim": d,
                    "prefix_tokens": w.P, "levels": list(w.levels), "tree": w.spec_name,
-                   "p_agree": w.p_agree, "splits": args.splits or "auto",
+                   "p_agree": w.p_agree, "prefix_workgroups": args.parts or "auto",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),

@@ -84,7 +84,9 @@ typedef struct {
   int32_t C;        /* block size: tokens per compressed entry (>= 1) */
   int32_t cap;      /* pool capacity in entries, a multiple of TV_POOL_ALIGN */
   void* k;          /* [B][Hkv][cap][d]  committed entries, row-major (entry-major) */
-  void* vt;         /* [B][Hkv][d][cap]  committed entries, TRANSPOSED (entry index fastest) */
+  void* vt;         /* [B][Hkv][cap/64][d][64] committed entries, transposed within each aligned
+                       block of 64 entries (entry j, channel c at [j/64][c][j%64]): a block of
+                       64 entries is one contiguous 64*d-element tile */
   int32_t* n;       /* [B] committed entries of each sequence (kept equal to P/C) */
   float* open_k;    /* [B][Hkv][d] fp32 sum of the committed tokens of the open block */
   float* open_v;    /* [B][Hkv][d] */
@@ -127,12 +129,15 @@ TV_API tv_status tv_build_tree_mask(int B, int D, const int32_t* parents, uint64
                                     int32_t* depth, int32_t* seq_err, hipStream_t stream);
 
 /*
- * Bytes of device workspace tv_verify_attn needs for this state shape, with
- * num_splits split-KV partitions (0 = the library's choice for the current device;
- * the same value must then be passed to tv_verify_attn).  Returns 0 on invalid
- * arguments.
+ * Bytes of device workspace tv_verify_attn needs for this state shape when the
+ * shared-prefix stream is cut into num_parts equal slices, one workgroup each
+ * (0 = the library's choice for the current device: one full round of resident
+ * workgroups; the same value must then be passed to tv_verify_attn).  The slices run
+ * over every (sequence, KV head, 64-query-row block) prefix laid end to end, so any
+ * batch size keeps the whole GPU busy; each slice leaves one partial (max, sum,
+ * unnormalised output) per prefix it touches.  Returns 0 on invalid arguments.
  */
-TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_splits);
+TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_parts);
 
 /*
  * Branch-aware causal verification (TSD-V4 §3.1: each candidate attends to the
@@ -149,7 +154,7 @@ TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, 
  *   anc, depth from tv_build_tree_mask; seq_err [B] in (NULL = all OK)
  *   scratch  out (NULL = do not build it); out [B][D][Hq][d] out (element dtype)
  *   lse      [B][D][Hq] fp32 out, natural-log softmax normaliser (NULL = not wanted)
- *   workspace: >= tv_verify_attn_workspace_bytes(D, Hq, st, num_splits) bytes
+ *   workspace: >= tv_verify_attn_workspace_bytes(D, Hq, st, num_parts) bytes, 16-byte aligned
  * Supported: d in {64, 128}; Hq % Hkv == 0; TV_BF16 with d = 128 runs the MFMA
  * kernel, everything else the fp32 vector kernel.
  */
@@ -157,7 +162,7 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
                                 const void* v_tree, const uint64_t* anc, const int32_t* depth,
                                 const int32_t* seq_err, const tv_state* st,
                                 const tv_scratch* scratch, void* out, float* lse,
-                                void* workspace, size_t workspace_bytes, int num_splits,
+                                void* workspace, size_t workspace_bytes, int num_parts,
                                 hipStream_t stream);
 
 /*

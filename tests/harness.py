@@ -90,14 +90,14 @@ def device_state(w: synth.Workload, caps: List[int], poison: bool = False):
     import concurrent.futures as cf
 
     def draw(b):
-        return [(k, np.ascontiguousarray(v.transpose(0, 2, 1))) for k, v in synth.pooled_prefix(w, b)]
+        return [(k, tv.tv.tile_vt(v, st.caps[l])) for l, (k, v) in enumerate(synth.pooled_prefix(w, b))]
 
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
         for b, lv in enumerate(ex.map(draw, range(w.B))):
             for l, (k, vt) in enumerate(lv):
                 n = k.shape[1]
                 st.pool_k[l][b, :, :n] = tv.to_device(k, w.dtype)
-                st.pool_vt[l][b, :, :, :n] = tv.to_device(vt, w.dtype)
+                st.pool_vt[l][b] = tv.to_device(vt, w.dtype)
                 st.n[l][b] = n
     st.P.fill_(w.P)
     torch.cuda.synchronize()
@@ -125,7 +125,7 @@ def upload_step(s: synth.StepInputs, dtype: str) -> DevStep:
 class Runner:
     """Owns the per-step device buffers of one (B, D, Hq) shape and runs the four calls."""
 
-    def __init__(self, st, D: int, Hq: int, num_splits: int = 0):
+    def __init__(self, st, D: int, Hq: int, num_parts: int = 0):
         import torch
         import tree_speculative_decoding_amd as tv
         self.st, self.D, self.Hq = st, D, Hq
@@ -141,8 +141,8 @@ class Runner:
         self.bonus = torch.zeros(B, dtype=torch.int32, device=dev)
         self.log = torch.zeros(B, max(len(st.levels), 1), D, 2, dtype=torch.int32, device=dev)
         self.sc = tv.DeviceScratch(B, D, Hkv, d, st.dtype, len(st.levels))
-        self.num_splits = num_splits
-        nbytes = tv.tv_verify_attn_workspace_bytes(D, Hq, st, num_splits)
+        self.num_parts = num_parts
+        nbytes = tv.tv_verify_attn_workspace_bytes(D, Hq, st, num_parts)
         assert nbytes > 0
         self.ws = torch.empty(nbytes // 4 + 64, dtype=torch.float32, device=dev)
 
@@ -150,10 +150,10 @@ class Runner:
         import tree_speculative_decoding_amd as tv
         tv.tv_build_tree_mask(x.parents, self.anc, self.depth, self.err)
 
-    def attend(self, x: DevStep, num_splits: Optional[int] = None):
+    def attend(self, x: DevStep):
         import tree_speculative_decoding_amd as tv
         tv.tv_verify_attn(x.q, x.kt, x.vt, self.anc, self.depth, self.err, self.st, self.sc, self.out,
-                          self.lse, self.ws, self.num_splits if num_splits is None else num_splits)
+                          self.lse, self.ws, self.num_parts)
 
     def accept(self, x: DevStep):
         import tree_speculative_decoding_amd as tv
@@ -208,6 +208,7 @@ def compare_state(dst, ost: oracle.State, dtype: str, what: str = "", batch: Opt
     """Device state vs oracle state: counts and tail bit-exact, entries/open sums within
     tolerance.  ``batch`` maps oracle sequence k to device sequence batch[k];
     ``first_entry[l][k]`` limits the entry comparison to slots from there on."""
+    import tree_speculative_decoding_amd as tv
     bs = list(range(dst.B)) if batch is None else list(batch)
     P = dst.P.cpu().numpy()[bs]
     assert (P == ost.P).all(), f"{what} P {P} vs {ost.P}"
@@ -220,7 +221,7 @@ def compare_state(dst, ost: oracle.State, dtype: str, what: str = "", batch: Opt
             rk = ost.pool_k[l][k, :, lo:nb]
             rv = ost.pool_v[l][k, :, lo:nb]
             gk = host_f64(dst.pool_k[l][b, :, lo:nb].contiguous(), dtype)
-            gv = host_f64(dst.pool_vt[l][b, :, :, lo:nb].contiguous(), dtype).transpose(0, 2, 1)
+            gv = tv.tv.untile_vt(host_f64(dst.pool_vt[l][b], dtype))[:, lo:nb]
             assert (np.abs(gk - rk) <= entry_tol(dtype, rk)).all(), f"{what} level {l} seq {b} K entries"
             assert (np.abs(gv - rv) <= entry_tol(dtype, rv)).all(), f"{what} level {l} seq {b} V entries"
         ok_ = dst.open_k[l].cpu().numpy().astype(np.float64)[bs]

@@ -88,8 +88,9 @@ def test_verify_rejects_bad_levels_and_workspace():
     s = fake_state()
     assert L.tv_verify_attn(8, 15, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, 1 << 30, 1, None) == tv.TV_EINVAL  # Hq % Hkv
     need = L.tv_verify_attn_workspace_bytes(8, 16, ctypes.byref(s), 3)
-    # 2 seq x 2 heads x 3 splits x 64 rows x (128 + 2) floats, each part rounded to 256 B
-    assert need == 2 * 2 * 3 * 64 * 128 * 4 + 2 * 2 * 3 * 64 * 8
+    # 4 units (2 seq x 2 heads x 1 row block) of 2 + 2 chunks = 16 chunks in 3 slices of 6:
+    # a prefix meets at most 2 slices -> 2 partial slots of 64 rows x (128 + 2) floats
+    assert need == 2 * 2 * 2 * 64 * 128 * 4 + 2 * 2 * 2 * 64 * 8
     assert L.tv_verify_attn(8, 16, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, need - 1, 3, None) == tv.TV_EWORKSPACE
     assert L.tv_verify_attn_workspace_bytes(0, 16, ctypes.byref(s), 3) == 0
 

@@ -19,7 +19,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def run_verify(w, step=0, q_scale=1.0, num_splits=0, poison=True, mutate=None):
+def run_verify(w, step=0, q_scale=1.0, num_parts=0, poison=True, mutate=None):
     """Run plan + verify on the GPU and in the oracle for workload w; returns both sides."""
     import torch
     caps = pooled_caps(w, 64)
@@ -30,7 +30,7 @@ def run_verify(w, step=0, q_scale=1.0, num_splits=0, poison=True, mutate=None):
         mutate(s)
     h = widen_step(s, w.dtype)
     x = upload_step(s, w.dtype)
-    r = Runner(dst, w.D, w.Hq, num_splits)
+    r = Runner(dst, w.D, w.Hq, num_parts)
     r.plan(x)
     r.attend(x)
     torch.cuda.synchronize()
@@ -105,16 +105,18 @@ def test_verify_tree_dominant():
     assert np.abs(wrong - res["out"]).max() > 10 * ATT_ATOL["bf16"]
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 7, 33])
-def test_split_count_invariance(splits):
-    _say(f"verify splits={splits}")
-    check_outputs(run_verify(synth.WORKLOADS["linear"], num_splits=splits))
+@pytest.mark.parametrize("parts", [1, 2, 3, 7, 33, 1000])
+def test_partition_invariance(parts):
+    """Any cut of the prefix stream into workgroup slices gives the same result (within
+    tolerance): slices that start or end inside a prefix, several prefixes per slice."""
+    _say(f"verify parts={parts}")
+    check_outputs(run_verify(synth.WORKLOADS["linear"], num_parts=parts))
 
 
 def test_determinism_bit_identical():
     _say("verify determinism")
     import torch
-    res = run_verify(synth.WORKLOADS["tree"], num_splits=4)
+    res = run_verify(synth.WORKLOADS["tree"], num_parts=4)
     r, x = res["r"], res["x"]
     a = r.out.clone()
     l1 = r.lse.clone()

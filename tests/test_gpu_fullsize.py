@@ -33,7 +33,7 @@ def test_high_batch_full_size():
     s = synth.step_inputs(w, 0)
     x = upload_step(s, w.dtype)
     r = Runner(dst, w.D, w.Hq)  # auto split plan, as timed
-    _say(f"full size: step (splits plan {r.ws.numel() * 4} B workspace)")
+    _say(f"full size: step ({r.ws.numel() * 4} B workspace)")
     n_before = [dst.n[l].clone() for l in range(len(w.levels))]
     P_before = dst.P.clone()
     r.step(x)

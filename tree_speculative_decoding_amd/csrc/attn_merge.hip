@@ -38,10 +38,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 #pragma unroll
   for (int x = 0; x < EPL; ++x) o[x] = 0.f;
 
-  // split-KV partials of the shared prefix
+  // partials of the shared prefix: one per workgroup whose slice touched this row's unit
   const size_t bg = (size_t)b * a.Hkv + g;
-  for (int s = 0; s < a.splits; ++s) {
-    const size_t wrow = (bg * a.splits + s) * a.R + r;
+  const long long u = (long long)bg * a.row_blocks + r / 64;
+  const int n_parts = a.parts > 0 ? unit_part_count(u, a.tmax, a.per) : 0;
+  for (int s = 0; s < n_parts; ++s) {
+    const size_t wrow = (bg * a.smax + s) * a.R + r;
     const float2 ml = a.ws_ml[wrow];
     if (ml.y > 0.f) {
       const float mn = fmaxf(m, ml.x);

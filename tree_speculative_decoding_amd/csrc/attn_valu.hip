@@ -4,12 +4,12 @@
 // compressed history).  Used for fp32 inputs and for shapes the MFMA kernel does
 // not take (bf16 with head dim 64).
 //
-// Grid (split, KV head x row block, sequence); 256 threads = 64 query rows x 4.
-// The split's 64-entry chunks are streamed through LDS in 32-entry tiles (K
-// row-major, V kept transposed as in HBM); each row keeps an online-softmax
-// running max (base-2 units), a per-thread partial sum and a quarter of the
-// output row in registers.  The partial (max, sum, unnormalised output) goes to
-// the workspace for the merge kernel.
+// One persistent workgroup per slice of the units' chunks (as in the MFMA kernel);
+// 256 threads = 64 query rows x 4.  The 64-entry chunks are streamed through LDS in
+// 32-entry tiles (K row-major, V transposed as in HBM); each row keeps an
+// online-softmax running max (base-2 units), a per-thread partial sum and a quarter
+// of the output row in registers.  The partial (max, sum, unnormalised output) of
+// every unit goes to the workspace for the merge kernel.
 #include "tv_common.h"
 
 namespace tv {
@@ -24,108 +24,119 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   __shared__ float Vs[DH][TK + 1];
   __shared__ float Ps[RBLK][TK + 1];
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y % a.Hkv;
-  const int rb = blockIdx.y / a.Hkv;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int r_loc = tid >> 2, part = tid & 3;
-  const int row = rb * RBLK + r_loc;
   const T* q = (const T*)a.q;
 
-  for (int e = tid; e < RBLK * DH; e += 256) {
-    const int rr = e / DH, dd = e - rr * DH;
-    const int rw = rb * RBLK + rr;
-    float v = 0.f;
-    if (rw < a.R) {
-      const int i = rw / a.G, hh = rw - i * a.G;
-      v = Elem<T>::load(q, (((size_t)b * a.D + i) * a.Hq + g * a.G + hh) * DH + dd);
-    }
-    Qs[rr][dd] = v;
-  }
-
-  const bool live = a.seq_err == nullptr || a.seq_err[b] == TV_SEQ_OK;
-  const int n0 = a.n_levels > 0 ? level_count(a.pn[0], b, a.cap[0]) : 0;
-  const int n1 = a.n_levels > 1 ? level_count(a.pn[1], b, a.cap[1]) : 0;
-  const int T0 = (n0 + 63) / 64, T1 = (n1 + 63) / 64;
-  const int per = (T0 + T1 + a.splits - 1) / a.splits;
-  const int c_lo = s * per;
-  const int c_hi = live ? min(T0 + T1, c_lo + per) : c_lo;
-
-  float o[DQ];
-#pragma unroll
-  for (int x = 0; x < DQ; ++x) o[x] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  for (int c = c_lo; c < c_hi; ++c) {
-    int lvl, e0, cnt;
-    chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
-    const T* pk = (const T*)a.pk[lvl];
-    const T* pvt = (const T*)a.pvt[lvl];
+  const long long total = a.units * a.tmax;
+  long long cg = (long long)blockIdx.x * a.per;
+  const long long cend = min(cg + a.per, total);
+  while (cg < cend) {
+    const long long u = cg / a.tmax;
+    const int c_first = (int)(cg - u * a.tmax);
+    const int c_last = (int)min((long long)a.tmax, cend - u * a.tmax);
+    const int slot = (int)(blockIdx.x - unit_first_part(u, a.tmax, a.per));
+    const int rb = (int)(u % a.row_blocks);
+    const int g = (int)((u / a.row_blocks) % a.Hkv);
+    const int b = (int)(u / ((long long)a.row_blocks * a.Hkv));
     const size_t bg = (size_t)b * a.Hkv + g;
-    const int cap = a.cap[lvl];
-    for (int sub = 0; sub * TK < cnt; ++sub) {
-      const int base = e0 + sub * TK;
-      const int n_sub = min(TK, cnt - sub * TK);
-      __syncthreads();  // previous tile fully consumed (and Q staged on the first pass)
-      for (int e = tid; e < TK * DH; e += 256) {
-        const int k = e / DH, dd = e - k * DH;
-        Ks[k][dd] = k < n_sub ? Elem<T>::load(pk, (bg * cap + base + k) * DH + dd) : 0.f;
+    const int row = rb * RBLK + r_loc;
+
+    __syncthreads();  // the previous unit is done with Qs
+    for (int e = tid; e < RBLK * DH; e += 256) {
+      const int rr = e / DH, dd = e - rr * DH;
+      const int rw = rb * RBLK + rr;
+      float v = 0.f;
+      if (rw < a.R) {
+        const int i = rw / a.G, hh = rw - i * a.G;
+        v = Elem<T>::load(q, (((size_t)b * a.D + i) * a.Hq + g * a.G + hh) * DH + dd);
       }
-      for (int e = tid; e < DH * TK; e += 256) {
-        const int dd = e / TK, k = e - dd * TK;
-        Vs[dd][k] = k < n_sub ? Elem<T>::load(pvt, (bg * DH + dd) * cap + base + k) : 0.f;
-      }
-      __syncthreads();
-      float sc[TK / 4];
-      float tmax = -INFINITY;
+      Qs[rr][dd] = v;
+    }
+
+    const bool live = a.seq_err == nullptr || a.seq_err[b] == TV_SEQ_OK;
+    const int n0 = a.n_levels > 0 ? level_count(a.pn[0], b, a.cap[0]) : 0;
+    const int n1 = a.n_levels > 1 ? level_count(a.pn[1], b, a.cap[1]) : 0;
+    const int T0 = (n0 + 63) / 64, T1 = (n1 + 63) / 64;
+    const int c_lo = c_first;
+    const int c_hi = live ? min(c_last, T0 + T1) : c_first;
+
+    float o[DQ];
 #pragma unroll
-      for (int jj = 0; jj < TK / 4; ++jj) {
-        const int k = part + 4 * jj;
-        float acc = 0.f;
+    for (int x = 0; x < DQ; ++x) o[x] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int c = c_lo; c < c_hi; ++c) {
+      int lvl, e0, cnt;
+      chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
+      const T* pk = (const T*)a.pk[lvl];
+      const T* pvt = (const T*)a.pvt[lvl];
+      const int cap = a.cap[lvl];
+      for (int sub = 0; sub * TK < cnt; ++sub) {
+        const int base = e0 + sub * TK;
+        const int n_sub = min(TK, cnt - sub * TK);
+        __syncthreads();  // previous tile fully consumed (and Q staged on the first pass)
+        for (int e = tid; e < TK * DH; e += 256) {
+          const int k = e / DH, dd = e - k * DH;
+          Ks[k][dd] = k < n_sub ? Elem<T>::load(pk, (bg * cap + base + k) * DH + dd) : 0.f;
+        }
+        for (int e = tid; e < DH * TK; e += 256) {
+          const int dd = e / TK, k = e - dd * TK;
+          Vs[dd][k] = k < n_sub ? Elem<T>::load(pvt, vt_index(bg * cap * DH, base + k, dd, DH)) : 0.f;
+        }
+        __syncthreads();
+        float sc[TK / 4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int jj = 0; jj < TK / 4; ++jj) {
+          const int k = part + 4 * jj;
+          float acc = 0.f;
 #pragma unroll 8
-        for (int dd = 0; dd < DH; ++dd) acc = fmaf(Qs[r_loc][dd], Ks[k][dd], acc);
-        const float x = acc * a.scale_log2;
-        sc[jj] = k < n_sub ? x : -INFINITY;
-        tmax = fmaxf(tmax, sc[jj]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
-      const float m_new = fmaxf(m_run, tmax);  // finite: n_sub >= 1
-      const float alpha = exp2f(m_run - m_new);
-      float psum = 0.f;
+          for (int dd = 0; dd < DH; ++dd) acc = fmaf(Qs[r_loc][dd], Ks[k][dd], acc);
+          const float x = acc * a.scale_log2;
+          sc[jj] = k < n_sub ? x : -INFINITY;
+          tmax = fmaxf(tmax, sc[jj]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
+        const float m_new = fmaxf(m_run, tmax);  // finite: n_sub >= 1
+        const float alpha = exp2f(m_run - m_new);
+        float psum = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < TK / 4; ++jj) {
-        const int k = part + 4 * jj;
-        const float p = k < n_sub ? exp2f(sc[jj] - m_new) : 0.f;
-        Ps[r_loc][k] = p;
-        psum += p;
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      __syncthreads();
+        for (int jj = 0; jj < TK / 4; ++jj) {
+          const int k = part + 4 * jj;
+          const float p = k < n_sub ? exp2f(sc[jj] - m_new) : 0.f;
+          Ps[r_loc][k] = p;
+          psum += p;
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        __syncthreads();
 #pragma unroll
-      for (int x = 0; x < DQ; ++x) {
-        const int dd = part * DQ + x;
-        float acc = o[x] * alpha;
+        for (int x = 0; x < DQ; ++x) {
+          const int dd = part * DQ + x;
+          float acc = o[x] * alpha;
 #pragma unroll 8
-        for (int k = 0; k < TK; ++k) acc = fmaf(Ps[r_loc][k], Vs[dd][k], acc);
-        o[x] = acc;
+          for (int k = 0; k < TK; ++k) acc = fmaf(Ps[r_loc][k], Vs[dd][k], acc);
+          o[x] = acc;
+        }
       }
     }
-  }
-  l_run += __shfl_xor(l_run, 1, 64);
-  l_run += __shfl_xor(l_run, 2, 64);
-  if (row < a.R) {
-    const size_t w = (((size_t)b * a.Hkv + g) * a.splits + s) * a.R + row;
+    l_run += __shfl_xor(l_run, 1, 64);
+    l_run += __shfl_xor(l_run, 2, 64);
+    if (row < a.R) {
+      const size_t wr = (bg * a.smax + slot) * a.R + row;
 #pragma unroll
-    for (int x = 0; x < DQ; ++x) a.ws_o[w * DH + part * DQ + x] = o[x];
-    if (part == 0) a.ws_ml[w] = make_float2(m_run, l_run);
+      for (int x = 0; x < DQ; ++x) a.ws_o[wr * DH + part * DQ + x] = o[x];
+      if (part == 0) a.ws_ml[wr] = make_float2(m_run, l_run);
+    }
+    cg = u * a.tmax + c_last;
   }
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.splits, a.Hkv * a.row_blocks, a.B), block(256);
+  if (a.parts == 0) return hipSuccess;
+  dim3 grid(a.parts), block(256);
   if (a.dtype == TV_BF16) {
     if (a.d == 128)
       hipLaunchKernelGGL((k_attn_valu<uint16_t, 128>), grid, block, 0, s, a);

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_compress_entries(tv_state st, int l, co
     sv += Elem<T>::load(raw_v, o);
   }
   Elem<T>::store((T*)st.lvl[l].k, (((size_t)b * st.Hkv + g) * cap + j) * d + dd, sk / (float)C);
-  Elem<T>::store((T*)st.lvl[l].vt, (((size_t)b * st.Hkv + g) * d + dd) * cap + j, sv / (float)C);
+  Elem<T>::store((T*)st.lvl[l].vt, vt_index(((size_t)b * st.Hkv + g) * cap * d, j, dd, d), sv / (float)C);
 }
 
 template <typename T>

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_refresh(int D, tv_state st, tv_scratch 
         const int g = e / d, dd = e - g * d;
         const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
         pk[(((size_t)b * Hkv + g) * cap + j) * d + dd] = ek[src];
-        pvt[(((size_t)b * Hkv + g) * d + dd) * cap + j] = ev[src];
+        pvt[vt_index(((size_t)b * Hkv + g) * cap * d, j, dd, d)] = ev[src];
       }
       if (commit_log != nullptr && tid == 0) {
         int32_t* row = commit_log + (((size_t)b * L + l) * D + (j - j0)) * 2;

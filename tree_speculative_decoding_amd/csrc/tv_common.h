@@ -52,6 +52,12 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// element offset of entry j, channel c of one (sequence, KV head) slice of a V pool
+// (64-entry tiles, transposed inside a tile)
+__device__ __forceinline__ size_t vt_index(size_t slice_base, int j, int c, int d) {
+  return slice_base + ((size_t)(j & ~63) * d) + (size_t)c * 64 + (j & 63);
+}
+
 // bits of the nodes 0..D-1 of a tree
 __device__ __forceinline__ uint64_t node_mask(int D) { return D >= 64 ? ~0ull : ((1ull << D) - 1ull); }
 
@@ -89,11 +95,19 @@ struct AttnArgs {
   float* lse;                        // may be null
   tv_scratch scratch;                // entries may be null
   int build_scratch;
-  int splits;                        // split-KV partitions per (sequence, KV head, row block)
-  int row_blocks;                    // ceil(R / 64)
-  int tiles_cap;                     // upper bound of 64-entry tiles over all levels
-  float* ws_o;                       // [B][Hkv][splits][R][d]
-  float2* ws_ml;                     // [B][Hkv][splits][R] (running max in log2 units, sum)
+  // Prefix-stream partition.  A unit is one (sequence, KV head, 64-row block); its prefix
+  // is `tmax` 64-entry chunks long (a bound from the pool capacities; chunks past a
+  // sequence's committed entries are empty).  The units' chunks, laid end to end, are cut
+  // into `parts` equal slices of `per` chunks, one workgroup each; a workgroup writes one
+  // partial per unit its slice touches, in slot (workgroup - first workgroup of the unit).
+  int row_blocks;                    // RB = ceil(R / 64)
+  int tmax;                          // chunks per unit
+  long long units;                   // B * Hkv * RB
+  int parts;                         // workgroups of the prefix stream
+  long long per;                     // chunks per workgroup
+  int smax;                          // partial slots per unit
+  float* ws_o;                       // [B][Hkv][smax][R][d]
+  float2* ws_ml;                     // [B][Hkv][smax][R] (running max in log2 units, sum)
   float scale_log2;                  // log2(e) / sqrt(d)
 };
 
@@ -112,6 +126,14 @@ __device__ __forceinline__ void chunk_entries(int n0, int T0, int n1, int c, int
     *e0 = (c - T0) * 64;
     *cnt = min(64, n1 - (c - T0) * 64);
   }
+}
+
+// first workgroup whose slice touches unit u, and how many workgroups touch it
+__device__ __forceinline__ long long unit_first_part(long long u, int tmax, long long per) {
+  return u * tmax / per;
+}
+__device__ __forceinline__ int unit_part_count(long long u, int tmax, long long per) {
+  return (int)((u * tmax + tmax - 1) / per - u * tmax / per + 1);
 }
 
 hipError_t launch_tree_mask(int B, int D, const int32_t* parents, uint64_t* anc, int32_t* depth,

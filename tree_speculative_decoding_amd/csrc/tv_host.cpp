@@ -72,46 +72,49 @@ int device_cus() {
 }
 
 struct Plan {
-  int R, row_blocks, tiles_cap, splits;
+  int R, row_blocks, tmax, parts, smax;
+  long long units, per;
   size_t ws_o_bytes, ws_ml_off, total;
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Split-KV plan.  Every (sequence, KV head, 64-row block) is a unit whose prefix is
-// streamed by `splits` workgroups.  Auto mode picks the split count that minimises the
-// modelled time: the workgroups run in ceil(units*splits / slots) rounds of equal
-// length (slots = CUs x resident workgroups per CU), and every split adds its partial
-// rows (written once, read once by the merge) to the bytes each unit streams.
-Plan make_plan(int D, int Hq, const tv_state* st, int num_splits) {
+// Prefix-stream partition (see AttnArgs).  Auto mode runs one round of persistent
+// workgroups, as many as fit on the device at once (two per CU for both kernels), but
+// keeps at least 16 chunks (1024 entries) per workgroup so that the partials stay a few
+// percent of the streamed bytes.
+Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   Plan p{};
   const int G = Hq / st->Hkv;
   p.R = G * D;
   p.row_blocks = (p.R + 63) / 64;
-  p.tiles_cap = 0;
-  for (int l = 0; l < st->n_levels; ++l) p.tiles_cap += (st->lvl[l].cap + 63) / 64;
-  if (num_splits > 0) {
-    p.splits = num_splits;
+  p.tmax = 0;
+  for (int l = 0; l < st->n_levels; ++l) p.tmax += (st->lvl[l].cap + 63) / 64;
+  p.units = (long long)st->B * st->Hkv * p.row_blocks;
+  const long long total = p.units * p.tmax;
+  if (total == 0) {
+    p.parts = 0;
+    p.per = 1;
+    p.smax = 0;
   } else {
-    const bool mfma = st->dtype == TV_BF16 && st->d == 128;
-    const double slots = (double)device_cus() * (mfma ? 3 : 1);
-    const double units = (double)st->B * st->Hkv * p.row_blocks;
-    const double esz = st->dtype == TV_BF16 ? 2.0 : 4.0;
-    const double unit_bytes = (double)p.tiles_cap * 64 * st->d * 2 * esz + 1.0;
-    const double partial_bytes = 2.0 * 64 * (st->d + 2) * 4;  // one split's rows, written + read
-    const int max_s = p.tiles_cap / 8 > 1 ? p.tiles_cap / 8 : 1;  // >= 8 chunks per split
-    double best = 1e300;
-    p.splits = 1;
-    for (int s = 1; s <= max_s && s <= 256; ++s) {
-      const double rounds = std::ceil(units * s / slots);
-      const double cost = rounds * (unit_bytes / s + partial_bytes);
-      if (cost < best * 0.999) {
-        best = cost;
-        p.splits = s;
-      }
+    long long want;
+    if (num_parts > 0) {
+      want = num_parts;
+    } else {
+      want = (long long)device_cus() * 2;
+      const long long by_size = (total + 15) / 16;
+      if (want > by_size) want = by_size;
     }
+    if (want > total) want = total;
+    if (want < 1) want = 1;
+    p.per = (total + want - 1) / want;
+    p.parts = (int)((total + p.per - 1) / p.per);
+    // a unit starting at offset o < per inside a slice meets floor((o + tmax - 1)/per) + 1 slices
+    long long sm = (p.per + p.tmax - 2) / p.per + 1;
+    if (sm > p.parts) sm = p.parts;
+    p.smax = (int)sm;
   }
-  const size_t rows = (size_t)st->B * st->Hkv * p.splits * p.R;
+  const size_t rows = (size_t)st->B * st->Hkv * p.smax * p.R;
   p.ws_o_bytes = round256(rows * st->d * sizeof(float));
   p.ws_ml_off = p.ws_o_bytes;
   p.total = p.ws_o_bytes + round256(rows * sizeof(float2));
@@ -153,23 +156,23 @@ TV_API tv_status tv_build_tree_mask(int B, int D, const int32_t* parents, uint64
   return hip_check(tv::launch_tree_mask(B, D, parents, anc, depth, seq_err, stream), "tree mask launch");
 }
 
-TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_splits) {
-  if (D < 1 || D > TV_MAX_D || Hq < 1 || num_splits < 0) return 0;
+TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_parts) {
+  if (D < 1 || D > TV_MAX_D || Hq < 1 || num_parts < 0) return 0;
   if (check_state(st) != TV_OK) return 0;
   if (Hq % st->Hkv != 0) return 0;
-  return make_plan(D, Hq, st, num_splits).total;
+  return make_plan(D, Hq, st, num_parts).total;
 }
 
 TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree, const void* v_tree,
                                 const uint64_t* anc, const int32_t* depth, const int32_t* seq_err,
                                 const tv_state* st, const tv_scratch* scratch, void* out, float* lse,
-                                void* workspace, size_t workspace_bytes, int num_splits,
+                                void* workspace, size_t workspace_bytes, int num_parts,
                                 hipStream_t stream) {
   tv_status s = check_state(st);
   if (s != TV_OK) return s;
   if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
   if (Hq < 1 || Hq % st->Hkv != 0) return fail(TV_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, st->Hkv);
-  if (num_splits < 0) return fail(TV_EINVAL, "num_splits = %d < 0", num_splits);
+  if (num_parts < 0) return fail(TV_EINVAL, "num_parts = %d < 0", num_parts);
   if (st->B == 0) return ok();
   if (!q || !k_tree || !v_tree || !anc || !depth || !out) return fail(TV_EINVAL, "NULL pointer argument");
   if (!aligned16(q)) return fail(TV_EINVAL, "q must be 16-byte aligned");
@@ -177,7 +180,7 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
     for (int l = 0; l < st->n_levels; ++l)
       if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
         return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
-  const Plan p = make_plan(D, Hq, st, num_splits);
+  const Plan p = make_plan(D, Hq, st, num_parts);
   if (workspace == nullptr || workspace_bytes < p.total)
     return fail(TV_EWORKSPACE, "workspace %zu bytes, need %zu", workspace == nullptr ? (size_t)0 : workspace_bytes,
                 p.total);
@@ -196,7 +199,8 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
   a.out = out; a.lse = lse;
   if (scratch != nullptr) a.scratch = *scratch;
   a.build_scratch = scratch != nullptr;
-  a.splits = p.splits; a.row_blocks = p.row_blocks; a.tiles_cap = p.tiles_cap;
+  a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
+  a.smax = p.smax;
   a.ws_o = (float*)workspace;
   a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
   a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);

@@ -137,6 +137,22 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
+def tile_vt(v: np.ndarray, cap: int) -> np.ndarray:
+    """Entry-major V rows [..., n, d] -> the pool's tiled transposed layout [..., cap/64, d, 64]
+    (entries n..cap-1 zero).  Layout conversion only."""
+    *lead, n, d = v.shape
+    full = np.zeros((*lead, cap, d), dtype=v.dtype)
+    full[..., :n, :] = v
+    t = full.reshape(*lead, cap // TV_POOL_ALIGN, TV_POOL_ALIGN, d)
+    return np.ascontiguousarray(np.swapaxes(t, -1, -2))
+
+
+def untile_vt(vt: np.ndarray) -> np.ndarray:
+    """Inverse of tile_vt: [..., cap/64, d, 64] -> [..., cap, d]."""
+    *lead, nt, d, w = vt.shape
+    return np.swapaxes(vt, -1, -2).reshape(*lead, nt * w, d)
+
+
 def round_cap(n: int) -> int:
     return max(TV_POOL_ALIGN, -(-n // TV_POOL_ALIGN) * TV_POOL_ALIGN)
 
@@ -155,7 +171,7 @@ class DeviceState:
         td = torch_dtype(dtype)
         z = lambda *s, dt=td: torch.zeros(*s, dtype=dt, device=device)
         self.pool_k = [z(B, Hkv, c, d) for c in self.caps]
-        self.pool_vt = [z(B, Hkv, d, c) for c in self.caps]
+        self.pool_vt = [z(B, Hkv, c // TV_POOL_ALIGN, d, TV_POOL_ALIGN) for c in self.caps]
         self.n = [z(B, dt=torch.int32) for _ in self.levels]
         self.open_k = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
         self.open_v = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
@@ -212,15 +228,15 @@ def tv_build_tree_mask(parents: torch.Tensor, anc: torch.Tensor, depth: torch.Te
                                     _stream(stream)))
 
 
-def tv_verify_attn_workspace_bytes(D: int, Hq: int, st, num_splits: int = 0) -> int:
+def tv_verify_attn_workspace_bytes(D: int, Hq: int, st, num_parts: int = 0) -> int:
     s = _state(st)
-    return int(lib().tv_verify_attn_workspace_bytes(D, Hq, ctypes.byref(s), num_splits))
+    return int(lib().tv_verify_attn_workspace_bytes(D, Hq, ctypes.byref(s), num_parts))
 
 
 def tv_verify_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, anc: torch.Tensor,
                    depth: torch.Tensor, seq_err: Optional[torch.Tensor], st, scratch,
                    out: torch.Tensor, lse: Optional[torch.Tensor], workspace: torch.Tensor,
-                   num_splits: int = 0, stream=None) -> None:
+                   num_parts: int = 0, stream=None) -> None:
     B, D, Hq, d = q.shape
     s = _state(st)
     sc = scratch.struct() if isinstance(scratch, DeviceScratch) else scratch
@@ -228,7 +244,7 @@ def tv_verify_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, 
                                 _ptr(seq_err), ctypes.byref(s),
                                 ctypes.byref(sc) if sc is not None else None, _ptr(out), _ptr(lse),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                num_splits, _stream(stream)))
+                                num_parts, _stream(stream)))
 
 
 def tv_accept(parents, anc, depth, draft_tok, target_tok, seq_err, m, path, bonus, stream=None) -> None:
