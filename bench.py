@@ -9,9 +9,10 @@ before timing; the persistent state evolves from step to step as it would while
 decoding.  Prints one JSON line:
 
   value          verified tree tokens per second (B*D per step / step time)
-  roofline       the prefix-stream attention kernel: algorithmic bytes per launch
-                 (every committed pool entry's K and V once, plus Q) over its
-                 average launch time from HIP events on its stream, vs 8 TB/s
+  roofline       the attention kernel (prefix stream + tail + chain): algorithmic
+                 bytes per launch (every committed pool entry's K and V once, the
+                 tail, Q, O, tree K/V, plan) over its average launch time from HIP
+                 events on its stream, vs 8 TB/s
   cpu_baseline   the fp64 oracle timed on this host for a bounded sample of the
                  same workload (rank 0, N = 1 only)
 """
@@ -181,10 +182,15 @@ def main():
     n_sum_after = sum(int(x.sum()) for x in st.n)
     accepted = (st.P - P_before).double().mean().item() / args.steps  # mean m + 1 per step
 
-    # algorithmic bytes of the prefix kernel per launch: every committed entry's K and V
-    # (averaged over the timed steps as the pools grow) plus the queries
+    # Algorithmic bytes of the attention kernel per launch: every committed entry's K and
+    # V once (averaged over the timed steps as the pools grow), the raw tail (< C0
+    # tokens), Q in, O out, the tree tokens' K and V, and the plan (parents, mask, depth:
+    # 16 B per node).  The prefix kernel reads all of these and writes every output row
+    # itself when each (sequence, head) prefix is one workgroup's whole slice.
     entries_per_seq_head = (n_sum_before + n_sum_after) / 2.0 / B
-    attn_bytes = B * Hkv * entries_per_seq_head * d * 2 * e + B * D * Hq * d * e
+    tail = float((P_before % w.levels[0]).float().mean().item()) if w.levels[0] > 1 else 0.0
+    attn_bytes = B * (Hkv * (entries_per_seq_head + tail) * d * 2 * e + D * Hq * d * 2 * e
+                      + D * Hkv * d * 2 * e + 16 * D)
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
     errs = int((err != 0).sum())
 
@@ -207,7 +213,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "k_attn_mfma (prefix stream)", "avg_launch_ms": round(attn_avg_ms, 5),
+                     "kernel": "k_attn_mfma (prefix stream + tail + chain)", "avg_launch_ms": round(attn_avg_ms, 5),
                      "algorithmic_bytes_per_launch": int(attn_bytes)},
         "accepted_length": round(accepted, 4),
         "seq_errors": errs,

@@ -184,6 +184,10 @@ EDGE = {
     "bf16_ragged": synth.Workload("e7", 3, 5, 40, 8, 128, "bf16", (4, 128), 4733, 2, 3, 0.6, 2007, prefix="raw"),
     # D = 64 chain
     "deep_chain": synth.Workload("e8", 1, 64, 8, 1, 128, "bf16", (4,), 100, 1, 63, 0.9, 2008, prefix="raw"),
+    # tail + tree = 2 + 24 entries: two 16-entry tiles in the prefix kernel's tree chunk
+    "tree_two_tiles": synth.Workload("e9", 2, 24, 16, 2, 128, "bf16", (4, 128), 1502, 3, 5, 0.6, 2009, prefix="raw"),
+    # tail + tree = 3 + 61 = 64 entries: the largest tree chunk, 6 row blocks
+    "tree_full_chunk": synth.Workload("e10", 1, 61, 8, 1, 128, "bf16", (4, 128), 1203, 4, 5, 0.6, 2010, prefix="raw"),
 }
 
 

@@ -1,123 +1,230 @@
-// Branch-aware verify attention, final step: merge the split-KV partials of the
-// shared prefix, add the finest level's raw tail and the node's own chain, and
-// normalise.  TSD-V4 §3.1: a candidate sees the accepted context and the
-// ancestors along its own branch, never candidates of other branches.
+// Branch-aware verify attention, final step, and the scratch pad.
 //
-// One wave64 per query row (sequence, node, head); each lane owns d/64 output
-// channels.  The chain is the node's ancestor mask: only its set bits are read,
-// so K/V of other branches never enter the arithmetic (excluded by selection,
-// not by a -inf score).  Everything is combined with the same base-2 online
-// softmax as the prefix kernels.
+// Attention (TSD-V4 §3.1: a candidate sees the accepted context and the ancestors on
+// its own branch, never candidates of other branches): merge the prefix-stream
+// partials of a query row, add the finest level's raw tail and the node's own chain,
+// and normalise.  Scratch pad (§4.1: chains share the prefix state but are compressed
+// independently after branching, one compression never mixes two chains; §4.2:
+// per-chain compressed tokens and intermediate sums stay in the scratch pad until
+// the path is accepted).
+//
+// One workgroup of 16 waves per (sequence, KV head, 64-row block).  The D tree tokens
+// of that KV head are staged once in LDS.  Each wave owns 4 query rows (rows
+// r = node * G + head-in-group) and each lane d/64 channels of a row; the chain is the node's
+// ancestor mask and only its set bits are read, so K/V of other branches never enter
+// the arithmetic (excluded by selection, not by a -inf score).  Chain scores are
+// reduced eight at a time with interleaved shuffles, then folded into the same
+// base-2 online softmax as the prefix kernels.  The row-block-0 workgroup of each
+// (sequence, KV head) also builds the scratch entries of that head: node i at
+// position pos = P + depth(i) sums, per level of block size C, the committed open sum
+// (only if its block began before the tree, b0 = floor(pos/C)*C < P) and its chain's
+// tokens at positions >= b0, in chain order, in fp32; a node ending a block writes
+// the entry sum/C (one rounding to the element type) and a zero open sum, any other
+// node the running sum.
 #include "tv_common.h"
 
 namespace tv {
 
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-  constexpr int EPL = DH / 64;
-  const int lane = threadIdx.x & 63;
-  const long row_id = (long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const long n_rows = (long)a.B * a.D * a.Hq;
-  if (row_id >= n_rows) return;
-  const int h = (int)(row_id % a.Hq);
-  const int i = (int)((row_id / a.Hq) % a.D);
-  const int b = (int)(row_id / ((long)a.Hq * a.D));
-  const int g = h / a.G;
-  const int r = i * a.G + (h - g * a.G);
-  const size_t obase = (((size_t)b * a.D + i) * a.Hq + h) * DH + lane * EPL;
+__global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
+  constexpr int EPL = DH / 64;  // channels per lane
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  T* kt_s = (T*)lds_raw;                         // [D][DH]
+  T* vt_s = kt_s + (size_t)a.D * DH;             // [D][DH]
+  int* dep_s = (int*)(vt_s + (size_t)a.D * DH);  // [D]
+
+  const int g = blockIdx.x % a.Hkv;
+  const int rb = blockIdx.x / a.Hkv;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const size_t bg = (size_t)b * a.Hkv + g;
+  const bool bad = a.seq_err != nullptr && a.seq_err[b] != TV_SEQ_OK;
   T* out = (T*)a.out;
 
-  if (a.seq_err != nullptr && a.seq_err[b] != TV_SEQ_OK) {
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) Elem<T>::store(out, obase + x, 0.f);
-    if (a.lse != nullptr && lane == 0) a.lse[((size_t)b * a.D + i) * a.Hq + h] = -INFINITY;
-    return;
+  // stage the tree tokens of this KV head and the depths
+  const T* ktg = (const T*)a.k_tree;
+  const T* vtg = (const T*)a.v_tree;
+  for (int e = tid; e < a.D * DH; e += blockDim.x) {
+    const int j = e / DH, c = e - j * DH;
+    const size_t o = (((size_t)b * a.D + j) * a.Hkv + g) * DH + c;
+    kt_s[e] = ktg[o];
+    vt_s[e] = vtg[o];
   }
+  for (int j = tid; j < a.D; j += blockDim.x) dep_s[j] = a.depth[(size_t)b * a.D + j];
+  __syncthreads();
 
-  float m = -INFINITY, l = 0.f, o[EPL];
-#pragma unroll
-  for (int x = 0; x < EPL; ++x) o[x] = 0.f;
-
-  // partials of the shared prefix: one per workgroup whose slice touched this row's unit
-  const size_t bg = (size_t)b * a.Hkv + g;
-  const long long u = (long long)bg * a.row_blocks + r / 64;
-  const int n_parts = a.parts > 0 ? unit_part_count(u, a.tmax, a.per) : 0;
-  for (int s = 0; s < n_parts; ++s) {
-    const size_t wrow = (bg * a.smax + s) * a.R + r;
-    const float2 ml = a.ws_ml[wrow];
-    if (ml.y > 0.f) {
-      const float mn = fmaxf(m, ml.x);
-      const float ca = exp2f(m - mn), cb = exp2f(ml.x - mn);
-      l = l * ca + ml.y * cb;
-#pragma unroll
-      for (int x = 0; x < EPL; ++x) o[x] = o[x] * ca + a.ws_o[wrow * DH + lane * EPL + x] * cb;
-      m = mn;
-    }
-  }
-
+  const uint64_t nodes = node_mask(a.D);
   const T* q = (const T*)a.q;
-  float qv[EPL];
+  for (int k = 0; k < 4; ++k) {
+    const int r = rb * 64 + w * 4 + k;
+    if (r >= a.R) break;  // wave-uniform
+    const int i = r / a.G, hh = r - i * a.G, h = g * a.G + hh;
+    const size_t obase = (((size_t)b * a.D + i) * a.Hq + h) * DH + lane * EPL;
+    if (bad) {
 #pragma unroll
-  for (int x = 0; x < EPL; ++x) qv[x] = Elem<T>::load(q, obase + x);
+      for (int x = 0; x < EPL; ++x) Elem<T>::store(out, obase + x, 0.f);
+      if (a.lse != nullptr && lane == 0) a.lse[((size_t)b * a.D + i) * a.Hq + h] = -INFINITY;
+      continue;
+    }
+    // partials of the shared prefix: one per workgroup whose slice touched this unit
+    const long long u = (long long)bg * a.row_blocks + rb;
+    const int n_parts = a.parts > 0 ? unit_part_count(u, a.tmax, a.per) : 0;
+    // with the tail and chain attended by the prefix kernel, a unit it covered with one
+    // workgroup is already written; otherwise its partials already hold tail and chain
+    if (a.fused_tree && n_parts == 1) continue;
+    float m = -INFINITY, l = 0.f, o[EPL];
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) o[x] = 0.f;
+    for (int s = 0; s < n_parts; ++s) {
+      const size_t wrow = (bg * a.smax + s) * a.R + r;
+      const float2 ml = a.ws_ml[wrow];
+      if (ml.y > 0.f) {
+        const float mn = fmaxf(m, ml.x);
+        const float ca = exp2f(m - mn), cb = exp2f(ml.x - mn);
+        l = l * ca + ml.y * cb;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) o[x] = o[x] * ca + a.ws_o[wrow * DH + lane * EPL + x] * cb;
+        m = mn;
+      }
+    }
 
-  auto absorb = [&](const T* kr, const T* vr) {
-    float part = 0.f;
+    float qv[EPL];
 #pragma unroll
-    for (int x = 0; x < EPL; ++x) part = fmaf(qv[x], Elem<T>::load(kr, lane * EPL + x), part);
-    const float sc = wave_sum(part) * a.scale_log2;
-    const float mn = fmaxf(m, sc);
-    const float ca = exp2f(m - mn), cb = exp2f(sc - mn);
-    l = l * ca + cb;
-#pragma unroll
-    for (int x = 0; x < EPL; ++x) o[x] = o[x] * ca + Elem<T>::load(vr, lane * EPL + x) * cb;
-    m = mn;
-  };
+    for (int x = 0; x < EPL; ++x) qv[x] = Elem<T>::load(q, obase + x);
 
-  // raw tokens of the finest level's open block
-  if (a.n_levels > 0 && a.C[0] > 1) {
-    const int C0 = a.C[0];
-    const int rr = a.P[b] % C0;
-    const T* tk = (const T*)a.tail_k;
-    const T* tv_ = (const T*)a.tail_v;
-    for (int t = 0; t < rr; ++t) {
-      const size_t off = (bg * (C0 - 1) + t) * DH;
-      absorb(tk + off, tv_ + off);
+    // raw tokens of the finest level's open block (at most C0 - 1 of them)
+    if (!a.fused_tree && a.n_levels > 0 && a.C[0] > 1) {
+      const int C0 = a.C[0];
+      const int rr = a.P[b] % C0;
+      const T* tk = (const T*)a.tail_k;
+      const T* tvv = (const T*)a.tail_v;
+      for (int t = 0; t < rr; ++t) {
+        const size_t off = (bg * (C0 - 1) + t) * DH + lane * EPL;
+        float part = 0.f;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) part = fmaf(qv[x], Elem<T>::load(tk, off + x), part);
+        const float sc = wave_sum(part) * a.scale_log2;
+        const float mn = fmaxf(m, sc);
+        const float ca = exp2f(m - mn), cb = exp2f(sc - mn);
+        l = l * ca + cb;
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) o[x] = o[x] * ca + Elem<T>::load(tvv, off + x) * cb;
+        m = mn;
+      }
+    }
+
+    // the node's own chain (ancestors and itself), eight nodes per round
+    uint64_t chain = a.fused_tree ? 0ull : a.anc[(size_t)b * a.D + i] & nodes;
+    while (chain != 0ull) {
+      int nj[8];
+      float sc[8];
+      int cnt = 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        nj[t] = chain != 0ull ? __builtin_ctzll(chain) : -1;
+        if (chain != 0ull) {
+          chain &= chain - 1ull;
+          ++cnt;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        float part = 0.f;
+        if (nj[t] >= 0) {
+#pragma unroll
+          for (int x = 0; x < EPL; ++x)
+            part = fmaf(qv[x], Elem<T>::load(kt_s, (size_t)nj[t] * DH + lane * EPL + x), part);
+        }
+        sc[t] = part;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) sc[t] += __shfl_xor(sc[t], off, 64);
+      float mx = m;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        sc[t] *= a.scale_log2;
+        if (t < cnt) mx = fmaxf(mx, sc[t]);
+      }
+      const float ca = exp2f(m - mx);
+      l *= ca;
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) o[x] *= ca;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < cnt) {
+          const float p = exp2f(sc[t] - mx);
+          l += p;
+#pragma unroll
+          for (int x = 0; x < EPL; ++x)
+            o[x] = fmaf(p, Elem<T>::load(vt_s, (size_t)nj[t] * DH + lane * EPL + x), o[x]);
+        }
+      }
+      m = mx;
+    }
+
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) Elem<T>::store(out, obase + x, o[x] * inv);
+    if (a.lse != nullptr && lane == 0) a.lse[((size_t)b * a.D + i) * a.Hq + h] = (m + log2f(l)) * kLn2;
+  }
+
+  // scratch pad of this KV head, once per (sequence, KV head); with the tail and chain
+  // attended by the prefix kernel, that kernel has built it
+  if (!a.build_scratch || a.fused_tree || rb != 0 || bad) return;
+  const int P = a.P[b];
+  const int HD = a.Hkv * DH;
+  for (int e = tid; e < a.D * DH; e += blockDim.x) {
+    const int i = e / DH, c = e - i * DH;
+    const uint64_t chain = a.anc[(size_t)b * a.D + i] & nodes;
+    const int pos = P + dep_s[i];
+    const size_t dst = ((size_t)b * a.D + i) * HD + (size_t)g * DH + c;
+    for (int lv = 0; lv < a.n_levels; ++lv) {
+      const int C = a.C[lv];
+      const int b0 = (pos / C) * C;
+      const size_t so = bg * DH + c;
+      float sk = b0 < P ? a.open_k[lv][so] : 0.f;
+      float sv = b0 < P ? a.open_v[lv][so] : 0.f;
+      uint64_t mm = chain;
+      while (mm != 0ull) {
+        const int j = __builtin_ctzll(mm);
+        mm &= mm - 1ull;
+        if (P + dep_s[j] >= b0) {
+          sk += Elem<T>::load(kt_s, (size_t)j * DH + c);
+          sv += Elem<T>::load(vt_s, (size_t)j * DH + c);
+        }
+      }
+      if ((pos + 1) % C == 0) {
+        Elem<T>::store((T*)a.scratch.entry_k[lv], dst, sk / (float)C);
+        Elem<T>::store((T*)a.scratch.entry_v[lv], dst, sv / (float)C);
+        a.scratch.open_k[lv][dst] = 0.f;
+        a.scratch.open_v[lv][dst] = 0.f;
+      } else {
+        a.scratch.open_k[lv][dst] = sk;
+        a.scratch.open_v[lv][dst] = sv;
+      }
     }
   }
-  // the node's own chain: ancestors and itself
-  uint64_t chain = a.anc[(size_t)b * a.D + i] & node_mask(a.D);
-  const T* kt = (const T*)a.k_tree;
-  const T* vt = (const T*)a.v_tree;
-  while (chain != 0ull) {
-    const int j = __builtin_ctzll(chain);
-    chain &= chain - 1ull;
-    const size_t off = (((size_t)b * a.D + j) * a.Hkv + g) * DH;
-    absorb(kt + off, vt + off);
-  }
-
-  const float inv = 1.0f / l;
-#pragma unroll
-  for (int x = 0; x < EPL; ++x) Elem<T>::store(out, obase + x, o[x] * inv);
-  if (a.lse != nullptr && lane == 0)
-    a.lse[((size_t)b * a.D + i) * a.Hq + h] = (m + log2f(l)) * kLn2;
 }
 
-hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s) {
-  const long rows = (long)a.B * a.D * a.Hq;
-  if (rows == 0) return hipSuccess;
-  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  if (a.dtype == TV_BF16) {
-    if (a.d == 128)
-      hipLaunchKernelGGL((k_attn_merge<uint16_t, 128>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((k_attn_merge<uint16_t, 64>), grid, block, 0, s, a);
-  } else {
-    if (a.d == 128)
-      hipLaunchKernelGGL((k_attn_merge<float, 128>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((k_attn_merge<float, 64>), grid, block, 0, s, a);
+template <typename T, int DH>
+static hipError_t launch_finish_t(const AttnArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)a.D * DH * sizeof(T) * 2 + (size_t)a.D * sizeof(int);
+  if (lds > 65536) {  // beyond the default dynamic-LDS limit (fp32, d = 128, D > 32)
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_finish<T, DH>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
   }
+  dim3 grid(a.Hkv * a.row_blocks, a.B), block(1024);
+  hipLaunchKernelGGL((k_attn_finish<T, DH>), grid, block, lds, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_finish(const AttnArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  if (a.dtype == TV_BF16) return a.d == 128 ? launch_finish_t<uint16_t, 128>(a, s) : launch_finish_t<uint16_t, 64>(a, s);
+  return a.d == 128 ? launch_finish_t<float, 128>(a, s) : launch_finish_t<float, 64>(a, s);
 }
 
 }  // namespace tv

@@ -1,15 +1,13 @@
-// Branch-aware verify attention, shared-prefix stream: bf16 MFMA kernel (gfx950).
-// TSD-V4 §3.1 (each candidate attends to the accepted context; the tree part is
-// added by the merge kernel), §2.2 (the context is the multi-resolution
-// compressed history), §2.1 / §5.3 (verification of many candidates is
-// memory-bound at small batch: the prefix is read once for all G*D query rows of
-// a KV head).
+// Branch-aware verify attention: bf16 MFMA kernel (gfx950).
+// TSD-V4 §3.1 (each candidate attends to the accepted context and to the ancestors
+// on its own branch only), §2.2 (the context is the multi-resolution compressed
+// history), §2.1 / §5.3 (verification of many candidates is memory-bound at small
+// batch: the prefix is read once for all G*D query rows of a KV head).
 //
 // A unit is one (sequence, KV head, 64-row block); the units' prefixes, cut into
 // 64-entry chunks and laid end to end, are split into equal slices, one persistent
-// workgroup each (one round on the GPU; a workgroup writes a partial for every unit its
-// slice touches).  NW waves per workgroup, 16 query rows per wave (rows
-// r = node * G + head-in-group).  Per 64-entry chunk:
+// workgroup each (one round on the GPU).  NW waves per workgroup, 16 query rows per
+// wave (rows r = node * G + head-in-group).  Per 64-entry chunk:
 //   1. the K chunk (64 x 128, row-major) and the V^T tile (128 x 64; the V pool is
 //      stored transposed per 64-entry tile) are each one contiguous 16 KB block,
 //      loaded with 16-byte coalesced loads into registers two chunks ahead (two
@@ -17,24 +15,29 @@
 //      copies, padded rows);
 //   2. S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the K chunk is the A operand
 //      (16 entries x 32 channels per lane group), Q^T the B operand kept in
-//      registers for the whole kernel; the accumulator gives each lane one query
-//      row and 4 entries per 16-entry tile;
+//      registers; the accumulator gives each lane one query row and 4 entries per
+//      16-entry tile;
 //   3. online softmax in base-2 units: the row max is combined across the four
 //      lane groups by two xor shuffles; each lane keeps its own partial sum; the
 //      accumulators are rescaled only when some row's maximum moved;
 //   4. O^T += V^T P^T with the same MFMA: the transposed V chunk is the A operand
 //      (16 channels x 32 entries), stored in LDS in the entry order the softmax
 //      lanes hold so each operand is one conflict-free 16-byte read; P^T (bf16)
-//      is the B operand straight from registers, and the
-//      accumulator again gives each lane its own query row, so the rescale by
-//      exp2(m_old - m_new) needs no data movement.
-// The unnormalised output rows, running max and sum go to the workspace.
+//      is the B operand straight from registers, and the accumulator again gives
+//      each lane its own query row, so the rescale needs no data movement.
+// The workgroup whose slice holds a unit's first chunk also attends to one more chunk
+// built from the finest level's raw tail and the tree tokens of the unit's KV head;
+// there a row sees the tail and exactly the nodes of its own chain (bits of the
+// node's ancestor mask), everything else is excluded by selection; from the same LDS
+// copy it builds that head's scratch pad.  If that workgroup's slice covers the whole
+// unit it normalises and writes the output rows and their LSE; otherwise every
+// workgroup of the unit writes a partial (running max, sum, unnormalised output) for
+// the merge kernel.
 #include "tv_common.h"
 
 namespace tv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
@@ -51,13 +54,25 @@ __device__ __forceinline__ int v_slot(int e) {
 }
 }  // namespace
 
-// At most 256 VGPRs: two workgroups per CU, each with two chunks (64 KB) in flight.
-template <int NW>
+// 16 KB of zeros: the load target of chunk slots past the end of a unit's stream.  Every
+// slot's loads are then issued unconditionally, so the wait before a chunk is written to
+// LDS counts exactly the loads issued after it and the next chunk stays in flight.
+static __device__ __attribute__((aligned(256))) uint4 g_zero_chunk[1024];
+
+// At most 256 VGPRs: two workgroups per CU, each with two chunks (64 KB) in flight.  TT is
+// the number of 16-entry tiles the tail + tree chunk takes (its registers are sized by it).
+template <int NW, int TT>
 __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int PER = (1024 + NT - 1) / NT;   // K pieces (and V pieces) per thread
   constexpr bool kFull = 1024 % NT == 0;
+  static_assert(TT >= 1 && TT <= 4, "the tail + tree chunk is at most 64 entries");
+  constexpr int TPER = (TT * 256 + NT - 1) / NT;  // its K (and V) pieces per thread
+  constexpr bool kTFull = (TT * 256) % NT == 0;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ int dep_s[TV_MAX_D];
+  __shared__ uint64_t anc_s[TV_MAX_D];
+  __shared__ float open_s[TV_MAX_LEVELS * 2 * kDH];
   char* Ks = smem;
   char* Vs = smem + kChunk * kKStr;
 
@@ -75,6 +90,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     const int c_first = (int)(cg - u * a.tmax);
     const int c_last = (int)min((long long)a.tmax, cend - u * a.tmax);
     const int slot = (int)(blockIdx.x - unit_first_part(u, a.tmax, a.per));
+    const bool whole_unit = c_first == 0 && c_last == a.tmax;  // no other workgroup touches it
     const int rb = (int)(u % a.row_blocks);
     const int g = (int)((u / a.row_blocks) % a.Hkv);
     const int b = (int)(u / ((long long)a.row_blocks * a.Hkv));
@@ -82,13 +98,14 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
 
     // Q^T operand: lane (n16, grp), k-step ks holds Q[row][32ks + 8grp .. +7]
     const int row = rb * 64 + w * 16 + n16;
+    const int node = row < a.R ? row / a.G : 0;
+    const int head = g * a.G + (row - node * a.G);
     const bool wave_has_rows = rb * 64 + w * 16 < a.R;  // wave-uniform
     bf16x8 qop[4];
     {
       const uint16_t* q = (const uint16_t*)a.q;
       if (row < a.R) {
-        const int i = row / a.G, hh = row - i * a.G;
-        const uint16_t* qr = q + (((size_t)b * a.D + i) * a.Hq + g * a.G + hh) * kDH;
+        const uint16_t* qr = q + (((size_t)b * a.D + node) * a.Hq + head) * kDH;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qop[ks] = *(const bf16x8*)(qr + 32 * ks + 8 * grp);
       } else {
@@ -97,9 +114,21 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
       }
     }
 
-    const bool live = a.seq_err == nullptr || a.seq_err[b] == TV_SEQ_OK;
-    const int n0 = a.n_levels > 0 ? level_count(a.pn[0], b, a.cap[0]) : 0;
-    const int n1 = a.n_levels > 1 ? level_count(a.pn[1], b, a.cap[1]) : 0;
+    // the sequence's error code, committed counts and prefix length in one round trip:
+    // lane 0 loads seq_err[b], lane 1 + l the count of level l, lane 3 P[b]
+    int uval = 0;
+    {
+      const int32_t* src = nullptr;
+      if (lane == 0) src = a.seq_err != nullptr ? a.seq_err + b : nullptr;
+      else if (lane == 1) src = a.n_levels > 0 ? a.pn[0] + b : nullptr;
+      else if (lane == 2) src = a.n_levels > 1 ? a.pn[1] + b : nullptr;
+      else if (lane == 3) src = a.P + b;
+      if (src != nullptr) uval = *src;
+    }
+    const bool live = a.seq_err == nullptr || __builtin_amdgcn_readlane(uval, 0) == TV_SEQ_OK;
+    const int n0 = a.n_levels > 0 ? max(0, min(__builtin_amdgcn_readlane(uval, 1), a.cap[0])) : 0;
+    const int n1 = a.n_levels > 1 ? max(0, min(__builtin_amdgcn_readlane(uval, 2), a.cap[1])) : 0;
+    const int Pb = __builtin_amdgcn_readlane(uval, 3);
     const int T0 = (n0 + 63) / 64, T1 = (n1 + 63) / 64;
     const int c_lo = c_first;
     const int c_hi = live ? min(c_last, T0 + T1) : c_first;
@@ -110,12 +139,17 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     // of a chunk are in bounds: every piece is loaded unconditionally (no data-dependent
     // code between the loads, so they are all in flight together) and entries past the
     // committed count are zeroed by selection when the chunk is written to LDS.
+    // Slots c >= c_hi (past the unit's stream) read the zero block.
     auto load_chunk = [&](int c, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
-      int lvl, e0, cnt;
-      chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
-      const uint32_t cap = (uint32_t)a.cap[lvl];
-      const char* kb = (const char*)a.pk[lvl] + (bg * cap + e0) * (kDH * 2);   // uniform
-      const char* vb = (const char*)a.pvt[lvl] + (bg * cap + e0) * (kDH * 2);  // uniform: V^T tile
+      const char* kb = (const char*)g_zero_chunk;
+      const char* vb = kb;
+      if (c < c_hi) {  // uniform
+        int lvl, e0, cnt;
+        chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
+        const uint32_t cap = (uint32_t)a.cap[lvl];
+        kb = (const char*)a.pk[lvl] + (bg * cap + e0) * (kDH * 2);   // K rows
+        vb = (const char*)a.pvt[lvl] + (bg * cap + e0) * (kDH * 2);  // V^T tile
+      }
 #pragma unroll
       for (int x = 0; x < PER; ++x) {
         const int p = tid + x * NT;
@@ -161,16 +195,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // one chunk: write it to LDS, refill its registers with the chunk two ahead, compute
-    auto step = [&](int c, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
-      int lvl, e0, cnt;
-      chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
-      __syncthreads();  // every wave is done reading the previous chunk
-      store_chunk(cnt, kpre, vpre);
-      __syncthreads();
-      if (c + 2 < c_hi) load_chunk(c + 2, kpre, vpre);  // in flight with chunk c + 1's loads
-      if (!wave_has_rows) return;
-
+    // Attend to the chunk in LDS.  hide(t, i) is true for the scores to leave out (entry
+    // 16t + 4grp + i of this lane's row); it is only evaluated when `masked`.
+    auto attend = [&](bool masked, auto hide) {
       // S^T tiles: sacc[t] lane (n16, grp) = S[row n16][entry 16t + 4grp + i]
       f32x4 sacc[4];
 #pragma unroll
@@ -182,15 +209,14 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
           sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ks], sacc[t], 0, 0, 0);
         }
       }
-      // Online softmax over this chunk, in base-2 units.  The scale is applied inside the
-      // exponent (one fma per score); the row max is taken on raw scores (scale > 0).
-      // Masking of uncommitted entries only happens in a partial chunk (uniform branch).
-      if (cnt < 64) {
+      // Online softmax in base-2 units.  The scale is applied inside the exponent (one
+      // fma per score); the row max is taken on raw scores (scale > 0).
+      if (masked) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (16 * t + 4 * grp + i >= cnt) sacc[t][i] = -INFINITY;
+            if (hide(t, i)) sacc[t][i] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                        fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
@@ -198,10 +224,12 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
                            fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);  // finite: cnt >= 1
+      // a row with every score hidden keeps its state (its max stays -inf, p = 0)
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
       // rows whose running max moved rescale their accumulators; skipped when none moved
       if (__ballot(m_new > m_run) != 0ull) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         l_run *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
@@ -214,39 +242,282 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           // exp2 of a non-positive argument; results below the normal range are flushed,
           // which cannot change a probability that is summed with at least one 1.0
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][i], a.scale_log2, -m_new));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][i], a.scale_log2, -m_use));
           l_run += p;
           pop[t >> 1][(t & 1) * 4 + i] = (__bf16)p;
         }
       }
-      // O^T += V^T P^T; k-step h covers entries 32h + {4grp..4grp+3} and 32h + 16 + {4grp..4grp+3}
+      // O^T += V^T P^T; k-step h: slots 32h + 8grp .. +7 hold entries 32h + 4grp + {0..3}
+      // and 32h + 16 + 4grp + {0..3}
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const char* vrow = Vs + (16 * dt + n16) * kVStr;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          // slots 32h + 8grp .. +7 hold entries 32h + 4grp + {0..3} and 32h + 16 + 4grp + {0..3}
           const bf16x8 vop = *(const bf16x8*)(vrow + (32 * h + 8 * grp) * 2);
           oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[h], oacc[dt], 0, 0, 0);
         }
       }
     };
 
-    if (c_lo < c_hi) load_chunk(c_lo, kpa, vpa);
-    if (c_lo + 1 < c_hi) load_chunk(c_lo + 1, kpb, vpb);
+    // One prefix chunk slot: if c is in the stream, write its chunk to LDS; refill the
+    // slot's registers with chunk c + 2 (always issued, so that it is in flight with
+    // chunk c + 1's loads); attend.
+    auto step = [&](int c, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
+      const bool have = c < c_hi;  // uniform
+      int cnt = 0;
+      if (have) {
+        int lvl, e0;
+        chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
+        __syncthreads();  // every wave is done reading the previous chunk
+        store_chunk(cnt, kpre, vpre);
+        __syncthreads();
+      }
+      load_chunk(c + 2, kpre, vpre);
+      if (!have || !wave_has_rows) return;
+      attend(cnt < 64, [&](int t, int i) { return 16 * t + 4 * grp + i >= cnt; });
+    };
+
+    // The unit's tail + chain chunk, attended first: entries [0, rr) are the finest level's
+    // raw tail (visible to every row), entries rr + j the tree node j of this KV head
+    // (visible to the rows of node i iff bit j of anc[i] is set).  Built by the workgroup
+    // holding the unit's first chunk.  Its global loads are issued before those of the
+    // first two prefix chunks, so that waiting for them leaves the prefix loads in flight
+    // while the chunk is attended (pieces of rows past the tail and the tree read node 0
+    // and are zeroed by selection).  Scores use the MFMA as below; the PV part runs on the
+    // vector ALU, each lane adding only the entries its row sees, so a value a row does
+    // not see is never multiplied (not even by a zero probability).
+    const bool tree_here = a.fused_tree && c_first == 0 && live;
+    const int C0 = a.n_levels > 0 ? a.C[0] : 1;
+    // Beyond its own loads (issued here) the stage reads only kernel arguments (constant
+    // level indices) and LDS: a vector load issued after the prefix loads would make its
+    // wait also wait for those.
+    const int rr = tree_here && C0 > 1 ? Pb % C0 : 0;
+    const int ne = rr + a.D;  // <= 16 * TT
+    char* Vr = Vs;  // V rows, entry-major, same padded stride as K (fits in the V^T area)
+    const bool want_scratch = tree_here && a.build_scratch && rb == 0;
+    uint4 tkp[TPER], tvp[TPER];
+    int dep_j = 0;
+    uint64_t anc_j = 0ull;
+    static_assert(NT >= kDH, "open-sum staging: one channel per thread");
+    float open_kv[TV_MAX_LEVELS][2] = {};  // committed open sums (K, V) of channel tid
+    if (tree_here) {
+      const uint16_t* tk = (const uint16_t*)a.tail_k;
+      const uint16_t* tvv = (const uint16_t*)a.tail_v;
+      const uint16_t* ktr = (const uint16_t*)a.k_tree;
+      const uint16_t* vtr = (const uint16_t*)a.v_tree;
+#pragma unroll
+      for (int x = 0; x < TPER; ++x) {
+        const int p = tid + x * NT;
+        const int e = p >> 4, col = p & 15;  // entry e, channels 8col .. 8col+7
+        const uint16_t* src_k;
+        const uint16_t* src_v;
+        if (e < rr) {
+          const size_t o = (bg * (C0 - 1) + e) * kDH + col * 8;
+          src_k = tk + o;
+          src_v = tvv + o;
+        } else {
+          const int j = e < ne ? e - rr : 0;
+          const size_t o = (((size_t)b * a.D + j) * a.Hkv + g) * kDH + col * 8;
+          src_k = ktr + o;
+          src_v = vtr + o;
+        }
+        if (kTFull || p < TT * 256) {
+          tkp[x] = *(const uint4*)src_k;
+          tvp[x] = *(const uint4*)src_v;
+        }
+      }
+      if (tid < a.D) {
+        dep_j = a.depth[(size_t)b * a.D + tid];
+        anc_j = a.anc[(size_t)b * a.D + tid];
+      }
+#pragma unroll
+      for (int lv = 0; lv < TV_MAX_LEVELS; ++lv)
+        if (want_scratch && lv < a.n_levels && tid < kDH) {
+          open_kv[lv][0] = a.open_k[lv][bg * kDH + tid];
+          open_kv[lv][1] = a.open_v[lv][bg * kDH + tid];
+        }
+    }
+
+    load_chunk(c_lo, kpa, vpa);
+    load_chunk(c_lo + 1, kpb, vpb);
+
+    if (tree_here) {
+      __syncthreads();  // every wave is done with the LDS of the previous unit
+#pragma unroll
+      for (int x = 0; x < TPER; ++x) {
+        const int p = tid + x * NT;
+        if (kTFull || p < TT * 256) {
+          const int e = p >> 4, col = p & 15;
+          const uint32_t ok = e < ne ? 0xffffffffu : 0u;
+          uint4 kv = tkp[x], vv = tvp[x];
+          kv.x &= ok; kv.y &= ok; kv.z &= ok; kv.w &= ok;
+          vv.x &= ok; vv.y &= ok; vv.z &= ok; vv.w &= ok;
+          *(uint4*)(Ks + e * kKStr + col * 16) = kv;
+          *(uint4*)(Vr + e * kKStr + col * 16) = vv;
+        }
+      }
+      if (tid < a.D) {
+        dep_s[tid] = dep_j;
+        anc_s[tid] = anc_j & node_mask(a.D);
+      }
+#pragma unroll
+      for (int lv = 0; lv < TV_MAX_LEVELS; ++lv)
+        if (want_scratch && lv < a.n_levels && tid < kDH) {
+          open_s[(lv * 2) * kDH + tid] = open_kv[lv][0];
+          open_s[(lv * 2 + 1) * kDH + tid] = open_kv[lv][1];
+        }
+      __syncthreads();
+      // Scratch pad of this KV head (once per sequence and head: the row-block-0 unit).
+      // TSD-V4 §4.1 / §4.2: node i at position pos = P + depth(i) sums, per level of block
+      // size C, the committed open sum (only if its block began before the tree,
+      // b0 = floor(pos/C)*C < P) and its own chain's tokens at positions >= b0, in chain
+      // order, in fp32; a node ending a block writes the entry sum/C (one rounding) and a
+      // zero open sum, any other node the running sum.  Other chains never enter.
+      if (want_scratch) {
+        const int P = Pb;
+        const int HD = a.Hkv * kDH;
+        for (int e = tid; e < a.D * kDH; e += NT) {
+          const int i = e / kDH, c = e - i * kDH;
+          const int pos = P + dep_s[i];
+          const uint64_t chain = anc_s[i];
+          const size_t dst = ((size_t)b * a.D + i) * HD + (size_t)g * kDH + c;
+#pragma unroll
+          for (int lv = 0; lv < TV_MAX_LEVELS; ++lv) {
+            if (lv >= a.n_levels) break;
+            const int C = a.C[lv];
+            const int b0 = (pos / C) * C;
+            float sk = b0 < P ? open_s[(lv * 2) * kDH + c] : 0.f;
+            float sv = b0 < P ? open_s[(lv * 2 + 1) * kDH + c] : 0.f;
+            uint64_t mm = chain;
+            while (mm != 0ull) {
+              const int j = __builtin_ctzll(mm);
+              mm &= mm - 1ull;
+              if (P + dep_s[j] >= b0) {
+                sk += bf16_bits_to_f32(*(const uint16_t*)(Ks + (rr + j) * kKStr + c * 2));
+                sv += bf16_bits_to_f32(*(const uint16_t*)(Vr + (rr + j) * kKStr + c * 2));
+              }
+            }
+            if ((pos + 1) % C == 0) {
+              ((uint16_t*)a.scratch.entry_k[lv])[dst] = f32_to_bf16_bits(sk / (float)C);
+              ((uint16_t*)a.scratch.entry_v[lv])[dst] = f32_to_bf16_bits(sv / (float)C);
+              a.scratch.open_k[lv][dst] = 0.f;
+              a.scratch.open_v[lv][dst] = 0.f;
+            } else {
+              a.scratch.open_k[lv][dst] = sk;
+              a.scratch.open_v[lv][dst] = sv;
+            }
+          }
+        }
+      }
+      if (wave_has_rows) {
+        const uint64_t chain = row < a.R ? anc_s[node] : 0ull;
+        const uint64_t vis = (rr > 0 ? (1ull << rr) - 1ull : 0ull) | (rr < 64 ? chain << rr : 0ull);
+        f32x4 sacc[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 kop = *(const bf16x8*)(Ks + (16 * t + n16) * kKStr + (32 * ks + 8 * grp) * 2);
+            sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ks], sacc[t], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!((vis >> (16 * t + 4 * grp + i)) & 1ull)) sacc[t][i] = -INFINITY;  // selection
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx * a.scale_log2);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sacc[t][i] = __builtin_amdgcn_exp2f(fmaf(sacc[t][i], a.scale_log2, -m_use));
+            l_run += sacc[t][i];
+          }
+        // entries some row of this wave sees (wave-uniform)
+        uint32_t any_lo = (uint32_t)vis, any_hi = (uint32_t)(vis >> 32);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          any_lo |= (uint32_t)__shfl_xor((int)any_lo, off, 64);
+          any_hi |= (uint32_t)__shfl_xor((int)any_hi, off, 64);
+        }
+        const uint64_t any = ((uint64_t)any_hi << 32) | any_lo;
+        // (vis, hence any, has no bit at or past ne); entry e = 16t + 4gp + i, whose
+        // probability for this lane's row is held by lane (n16, gp) in sacc[t][i]
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int gp = 0; gp < 4; ++gp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 16 * t + 4 * gp + i;
+          if (!((any >> e) & 1ull)) continue;
+          const float pe = __shfl(sacc[t][i], n16 + 16 * gp, 64);
+          if ((vis >> e) & 1ull) {
+            const char* vrow = Vr + e * kKStr;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+              const uint2 v4 = *(const uint2*)(vrow + (16 * dt + 4 * grp) * 2);
+              oacc[dt][0] = fmaf(pe, bf16_bits_to_f32(v4.x & 0xffffu), oacc[dt][0]);
+              oacc[dt][1] = fmaf(pe, bf16_bits_to_f32(v4.x >> 16), oacc[dt][1]);
+              oacc[dt][2] = fmaf(pe, bf16_bits_to_f32(v4.y & 0xffffu), oacc[dt][2]);
+              oacc[dt][3] = fmaf(pe, bf16_bits_to_f32(v4.y >> 16), oacc[dt][3]);
+            }
+          }
+        }
+      }
+    }
+
     for (int c = c_lo; c < c_hi; c += 2) {
       step(c, kpa, vpa);
-      if (c + 1 < c_hi) step(c + 1, kpb, vpb);
+      step(c + 1, kpb, vpb);
     }
 
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     if (row < a.R) {
-      const size_t wrow = ((bg * a.smax + slot) * a.R + row);
-      float* o = a.ws_o + wrow * kDH;
+      if (a.fused_tree && whole_unit) {
+        // the only workgroup of this unit: normalise and write the output rows
+        uint16_t* out = (uint16_t*)a.out;
+        const size_t obase = (((size_t)b * a.D + node) * a.Hq + head) * kDH;
+        if (live) {
+          const float inv = 1.0f / l_run;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(o + 16 * dt + 4 * grp) = oacc[dt];
-      if (grp == 0) a.ws_ml[wrow] = make_float2(m_run, l_run);
+          for (int dt = 0; dt < 8; ++dt) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16_bits(oacc[dt][0] * inv) | ((uint32_t)f32_to_bf16_bits(oacc[dt][1] * inv) << 16);
+            pk.y = (uint32_t)f32_to_bf16_bits(oacc[dt][2] * inv) | ((uint32_t)f32_to_bf16_bits(oacc[dt][3] * inv) << 16);
+            *(uint2*)(out + obase + 16 * dt + 4 * grp) = pk;
+          }
+          if (a.lse != nullptr && grp == 0)
+            a.lse[((size_t)b * a.D + node) * a.Hq + head] = (m_run + log2f(l_run)) * kLn2;
+        } else {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) *(uint2*)(out + obase + 16 * dt + 4 * grp) = make_uint2(0u, 0u);
+          if (a.lse != nullptr && grp == 0) a.lse[((size_t)b * a.D + node) * a.Hq + head] = -INFINITY;
+        }
+      } else {
+        const size_t wrow = ((bg * a.smax + slot) * a.R + row);
+        float* o = a.ws_o + wrow * kDH;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *(f32x4*)(o + 16 * dt + 4 * grp) = oacc[dt];
+        if (grp == 0) a.ws_ml[wrow] = make_float2(m_run, l_run);
+      }
     }
     cg = u * a.tmax + c_last;
   }
@@ -256,7 +527,10 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   // Always four waves: all of them load (32 KB per chunk), waves whose 16 rows are all
   // past the G*D query rows skip the arithmetic.  One workgroup per slice.
   if (a.parts == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_attn_mfma<4>, dim3(a.parts), dim3(256), 0, s, a);
+  const int tt = a.fused_tree ? a.tree_tiles : 1;
+  if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1>), dim3(a.parts), dim3(256), 0, s, a);
+  else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2>), dim3(a.parts), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_mfma<4, 4>), dim3(a.parts), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -4,7 +4,9 @@
 // state; rejected branches are not carried over) and §4.3 (C4 / C128 states and
 // their compression-intermediate buffers).
 //
-// One workgroup per sequence.  Every committed element is a bit copy: scratch
+// One workgroup per sequence, one thread per (KV head, channel) up to 1024; the
+// accepted path is staged in LDS and checked once.  Every committed element is a bit
+// copy: scratch
 // entries of the path nodes that close a block go to the next pool slots, the
 // path leaf's open-block sums replace the open sums, path tokens extend the raw
 // tail.  Counters (P, n) are written after a barrier, once every thread of the
@@ -14,13 +16,15 @@
 namespace tv {
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_refresh(int D, tv_state st, tv_scratch sc,
-                                                 const T* __restrict__ k_tree,
-                                                 const T* __restrict__ v_tree,
-                                                 const int32_t* __restrict__ m_in,
-                                                 const int32_t* __restrict__ path,
-                                                 int32_t* __restrict__ commit_log,
-                                                 int32_t* __restrict__ seq_err) {
+__global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch sc,
+                                                  const T* __restrict__ k_tree,
+                                                  const T* __restrict__ v_tree,
+                                                  const int32_t* __restrict__ m_in,
+                                                  const int32_t* __restrict__ path,
+                                                  int32_t* __restrict__ commit_log,
+                                                  int32_t* __restrict__ seq_err) {
+  __shared__ int pth[TV_MAX_D];
+  __shared__ int path_bad;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int L = st.n_levels;
@@ -30,12 +34,16 @@ __global__ __launch_bounds__(256) void k_refresh(int D, tv_state st, tv_scratch 
   const int err = seq_err[b];
   const int m = m_in[b];
   const int P = st.P[b];
+  if (tid == 0) path_bad = 0;
   __syncthreads();  // log prefill and the reads above happen before any later write
   if (err != TV_SEQ_OK || m < 0) return;
-  const int32_t* pth = path + (size_t)b * D;
-  bool bad = m >= D || P < 0;
-  for (int t = 0; t <= m && !bad; ++t) bad = pth[t] < 0 || pth[t] >= D;
-  if (bad) {
+  if (tid < D) {
+    const int v = path[(size_t)b * D + tid];
+    pth[tid] = v;
+    if (tid <= m && (v < 0 || v >= D)) atomicOr(&path_bad, 1);
+  }
+  __syncthreads();
+  if (m >= D || P < 0 || path_bad) {
     if (tid == 0) seq_err[b] = TV_SEQ_BAD_PATH;
     return;
   }
@@ -104,7 +112,7 @@ hipError_t launch_refresh(int D, const tv_state& st, const tv_scratch& sc, const
                           const void* v_tree, const int32_t* m, const int32_t* path,
                           int32_t* commit_log, int32_t* seq_err, hipStream_t s) {
   if (st.B == 0) return hipSuccess;
-  dim3 grid(st.B), block(256);
+  dim3 grid(st.B), block(st.Hkv * st.d >= 1024 ? 1024 : ((st.Hkv * st.d + 63) / 64) * 64);
   if (st.dtype == TV_BF16)
     hipLaunchKernelGGL(k_refresh<uint16_t>, grid, block, 0, s, D, st, sc, (const uint16_t*)k_tree,
                        (const uint16_t*)v_tree, m, path, commit_log, seq_err);

@@ -106,6 +106,9 @@ struct AttnArgs {
   int parts;                         // workgroups of the prefix stream
   long long per;                     // chunks per workgroup
   int smax;                          // partial slots per unit
+  int fused_tree;                    // the MFMA prefix kernel also attends to the raw tail and
+                                     // the tree chunk, and writes whole units' rows itself
+  int tree_tiles;                    // 16-entry tiles of that chunk: 1, 2 or 4
   float* ws_o;                       // [B][Hkv][smax][R][d]
   float2* ws_ml;                     // [B][Hkv][smax][R] (running max in log2 units, sum)
   float scale_log2;                  // log2(e) / sqrt(d)
@@ -149,7 +152,6 @@ hipError_t launch_compress(const tv_state& st, const void* raw_k, const void* ra
                            int32_t* seq_err, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_merge(const AttnArgs& a, hipStream_t s);
-hipError_t launch_scratch(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_finish(const AttnArgs& a, hipStream_t s);
 
 }  // namespace tv

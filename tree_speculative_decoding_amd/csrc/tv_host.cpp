@@ -201,11 +201,17 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
   a.build_scratch = scratch != nullptr;
   a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
   a.smax = p.smax;
+  const int c0 = st->n_levels > 0 ? st->lvl[0].C : 1;
   a.ws_o = (float*)workspace;
   a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
   a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);
 
   const bool mfma = st->dtype == TV_BF16 && st->d == 128;
+  // the tail (< C0 tokens) and the D tree tokens form one extra chunk of at most 64
+  // entries, attended in 16-entry tiles
+  const int tree_entries = D + (c0 - 1);
+  a.fused_tree = mfma && p.parts > 0 && tree_entries <= 64;
+  a.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
   if (g_ev_start) {
     s = hip_check(hipEventRecord(g_ev_start, stream), "timing event");
     if (s != TV_OK) return s;
@@ -216,10 +222,11 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
     s = hip_check(hipEventRecord(g_ev_stop, stream), "timing event");
     if (s != TV_OK) return s;
   }
-  s = hip_check(tv::launch_attn_merge(a, stream), "attention merge launch");
-  if (s != TV_OK) return s;
-  if (a.build_scratch) s = hip_check(tv::launch_scratch(a, stream), "scratch launch");
-  return s;
+  // nothing left for the finish kernel when the prefix kernel wrote every row (one
+  // workgroup per unit; it also builds the scratch pad)
+  const bool all_whole = a.fused_tree && p.per == p.tmax && (long long)p.parts == p.units;
+  if (all_whole) return ok();
+  return hip_check(tv::launch_attn_finish(a, stream), "attention finish launch");
 }
 
 TV_API tv_status tv_accept(int B, int D, const int32_t* parents, const uint64_t* anc, const int32_t* depth,
