@@ -18,7 +18,9 @@
  *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *    never allocates, frees or keeps a pointer after a call returns.  The
  *    tv_state / tv_scratch structs themselves are host structs passed by address;
- *    they are read during the call only.
+ *    they are read during the call only.  Arrays of elements or fp32 sums (Q, tree
+ *    K/V, pools, open sums, tails, scratch, the output, the workspace) must be
+ *    16-byte aligned: the kernels move them in 8- and 16-byte pieces.
  *  - Every call is asynchronous on `stream`; none synchronises the device or
  *    allocates, so the four-call step can be captured in a hipGraph.
  *  - Host-checkable argument errors return TV_EINVAL / TV_EUNSUPPORTED /

@@ -1,12 +1,7 @@
-// Branch-aware verify attention, final step, and the scratch pad.
-//
-// Attention (TSD-V4 §3.1: a candidate sees the accepted context and the ancestors on
-// its own branch, never candidates of other branches): merge the prefix-stream
-// partials of a query row, add the finest level's raw tail and the node's own chain,
-// and normalise.  Scratch pad (§4.1: chains share the prefix state but are compressed
-// independently after branching, one compression never mixes two chains; §4.2:
-// per-chain compressed tokens and intermediate sums stay in the scratch pad until
-// the path is accepted).
+// Branch-aware verify attention, final step (TSD-V4 §3.1: a candidate sees the accepted
+// context and the ancestors on its own branch, never candidates of other branches):
+// merge the prefix-stream partials of a query row, add the finest level's raw tail and
+// the node's own chain, and normalise.
 //
 // One workgroup of 16 waves per (sequence, KV head, 64-row block).  The D tree tokens
 // of that KV head are staged once in LDS.  Each wave owns 4 query rows (rows
@@ -14,13 +9,7 @@
 // ancestor mask and only its set bits are read, so K/V of other branches never enter
 // the arithmetic (excluded by selection, not by a -inf score).  Chain scores are
 // reduced eight at a time with interleaved shuffles, then folded into the same
-// base-2 online softmax as the prefix kernels.  The row-block-0 workgroup of each
-// (sequence, KV head) also builds the scratch entries of that head: node i at
-// position pos = P + depth(i) sums, per level of block size C, the committed open sum
-// (only if its block began before the tree, b0 = floor(pos/C)*C < P) and its chain's
-// tokens at positions >= b0, in chain order, in fp32; a node ending a block writes
-// the entry sum/C (one rounding to the element type) and a zero open sum, any other
-// node the running sum.
+// base-2 online softmax as the prefix kernels.
 #include "tv_common.h"
 
 namespace tv {
@@ -31,7 +20,6 @@ __global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   T* kt_s = (T*)lds_raw;                         // [D][DH]
   T* vt_s = kt_s + (size_t)a.D * DH;             // [D][DH]
-  int* dep_s = (int*)(vt_s + (size_t)a.D * DH);  // [D]
 
   const int g = blockIdx.x % a.Hkv;
   const int rb = blockIdx.x / a.Hkv;
@@ -41,7 +29,7 @@ __global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
   const bool bad = a.seq_err != nullptr && a.seq_err[b] != TV_SEQ_OK;
   T* out = (T*)a.out;
 
-  // stage the tree tokens of this KV head and the depths
+  // stage the tree tokens of this KV head
   const T* ktg = (const T*)a.k_tree;
   const T* vtg = (const T*)a.v_tree;
   for (int e = tid; e < a.D * DH; e += blockDim.x) {
@@ -50,7 +38,6 @@ __global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
     kt_s[e] = ktg[o];
     vt_s[e] = vtg[o];
   }
-  for (int j = tid; j < a.D; j += blockDim.x) dep_s[j] = a.depth[(size_t)b * a.D + j];
   __syncthreads();
 
   const uint64_t nodes = node_mask(a.D);
@@ -170,47 +157,11 @@ __global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
     if (a.lse != nullptr && lane == 0) a.lse[((size_t)b * a.D + i) * a.Hq + h] = (m + log2f(l)) * kLn2;
   }
 
-  // scratch pad of this KV head, once per (sequence, KV head); with the tail and chain
-  // attended by the prefix kernel, that kernel has built it
-  if (!a.build_scratch || a.fused_tree || rb != 0 || bad) return;
-  const int P = a.P[b];
-  const int HD = a.Hkv * DH;
-  for (int e = tid; e < a.D * DH; e += blockDim.x) {
-    const int i = e / DH, c = e - i * DH;
-    const uint64_t chain = a.anc[(size_t)b * a.D + i] & nodes;
-    const int pos = P + dep_s[i];
-    const size_t dst = ((size_t)b * a.D + i) * HD + (size_t)g * DH + c;
-    for (int lv = 0; lv < a.n_levels; ++lv) {
-      const int C = a.C[lv];
-      const int b0 = (pos / C) * C;
-      const size_t so = bg * DH + c;
-      float sk = b0 < P ? a.open_k[lv][so] : 0.f;
-      float sv = b0 < P ? a.open_v[lv][so] : 0.f;
-      uint64_t mm = chain;
-      while (mm != 0ull) {
-        const int j = __builtin_ctzll(mm);
-        mm &= mm - 1ull;
-        if (P + dep_s[j] >= b0) {
-          sk += Elem<T>::load(kt_s, (size_t)j * DH + c);
-          sv += Elem<T>::load(vt_s, (size_t)j * DH + c);
-        }
-      }
-      if ((pos + 1) % C == 0) {
-        Elem<T>::store((T*)a.scratch.entry_k[lv], dst, sk / (float)C);
-        Elem<T>::store((T*)a.scratch.entry_v[lv], dst, sv / (float)C);
-        a.scratch.open_k[lv][dst] = 0.f;
-        a.scratch.open_v[lv][dst] = 0.f;
-      } else {
-        a.scratch.open_k[lv][dst] = sk;
-        a.scratch.open_v[lv][dst] = sv;
-      }
-    }
-  }
 }
 
 template <typename T, int DH>
 static hipError_t launch_finish_t(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)a.D * DH * sizeof(T) * 2 + (size_t)a.D * sizeof(int);
+  const size_t lds = (size_t)a.D * DH * sizeof(T) * 2;
   if (lds > 65536) {  // beyond the default dynamic-LDS limit (fp32, d = 128, D > 32)
     hipError_t e = hipFuncSetAttribute((const void*)k_attn_finish<T, DH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -28,11 +28,10 @@
 // The workgroup whose slice holds a unit's first chunk also attends to one more chunk
 // built from the finest level's raw tail and the tree tokens of the unit's KV head;
 // there a row sees the tail and exactly the nodes of its own chain (bits of the
-// node's ancestor mask), everything else is excluded by selection; from the same LDS
-// copy it builds that head's scratch pad.  If that workgroup's slice covers the whole
-// unit it normalises and writes the output rows and their LSE; otherwise every
-// workgroup of the unit writes a partial (running max, sum, unnormalised output) for
-// the merge kernel.
+// node's ancestor mask), everything else is excluded by selection.  If that
+// workgroup's slice covers the whole unit it normalises and writes the output rows and
+// their LSE; otherwise every workgroup of the unit writes a partial (running max, sum,
+// unnormalised output) for the merge kernel.
 #include "tv_common.h"
 
 namespace tv {
@@ -70,9 +69,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int TPER = (TT * 256 + NT - 1) / NT;  // its K (and V) pieces per thread
   constexpr bool kTFull = (TT * 256) % NT == 0;
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  __shared__ int dep_s[TV_MAX_D];
   __shared__ uint64_t anc_s[TV_MAX_D];
-  __shared__ float open_s[TV_MAX_LEVELS * 2 * kDH];
   char* Ks = smem;
   char* Vs = smem + kChunk * kKStr;
 
@@ -295,12 +292,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     const int rr = tree_here && C0 > 1 ? Pb % C0 : 0;
     const int ne = rr + a.D;  // <= 16 * TT
     char* Vr = Vs;  // V rows, entry-major, same padded stride as K (fits in the V^T area)
-    const bool want_scratch = tree_here && a.build_scratch && rb == 0;
     uint4 tkp[TPER], tvp[TPER];
-    int dep_j = 0;
     uint64_t anc_j = 0ull;
-    static_assert(NT >= kDH, "open-sum staging: one channel per thread");
-    float open_kv[TV_MAX_LEVELS][2] = {};  // committed open sums (K, V) of channel tid
     if (tree_here) {
       const uint16_t* tk = (const uint16_t*)a.tail_k;
       const uint16_t* tvv = (const uint16_t*)a.tail_v;
@@ -328,15 +321,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
         }
       }
       if (tid < a.D) {
-        dep_j = a.depth[(size_t)b * a.D + tid];
         anc_j = a.anc[(size_t)b * a.D + tid];
       }
-#pragma unroll
-      for (int lv = 0; lv < TV_MAX_LEVELS; ++lv)
-        if (want_scratch && lv < a.n_levels && tid < kDH) {
-          open_kv[lv][0] = a.open_k[lv][bg * kDH + tid];
-          open_kv[lv][1] = a.open_v[lv][bg * kDH + tid];
-        }
     }
 
     load_chunk(c_lo, kpa, vpa);
@@ -358,58 +344,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
         }
       }
       if (tid < a.D) {
-        dep_s[tid] = dep_j;
         anc_s[tid] = anc_j & node_mask(a.D);
       }
-#pragma unroll
-      for (int lv = 0; lv < TV_MAX_LEVELS; ++lv)
-        if (want_scratch && lv < a.n_levels && tid < kDH) {
-          open_s[(lv * 2) * kDH + tid] = open_kv[lv][0];
-          open_s[(lv * 2 + 1) * kDH + tid] = open_kv[lv][1];
-        }
       __syncthreads();
-      // Scratch pad of this KV head (once per sequence and head: the row-block-0 unit).
-      // TSD-V4 §4.1 / §4.2: node i at position pos = P + depth(i) sums, per level of block
-      // size C, the committed open sum (only if its block began before the tree,
-      // b0 = floor(pos/C)*C < P) and its own chain's tokens at positions >= b0, in chain
-      // order, in fp32; a node ending a block writes the entry sum/C (one rounding) and a
-      // zero open sum, any other node the running sum.  Other chains never enter.
-      if (want_scratch) {
-        const int P = Pb;
-        const int HD = a.Hkv * kDH;
-        for (int e = tid; e < a.D * kDH; e += NT) {
-          const int i = e / kDH, c = e - i * kDH;
-          const int pos = P + dep_s[i];
-          const uint64_t chain = anc_s[i];
-          const size_t dst = ((size_t)b * a.D + i) * HD + (size_t)g * kDH + c;
-#pragma unroll
-          for (int lv = 0; lv < TV_MAX_LEVELS; ++lv) {
-            if (lv >= a.n_levels) break;
-            const int C = a.C[lv];
-            const int b0 = (pos / C) * C;
-            float sk = b0 < P ? open_s[(lv * 2) * kDH + c] : 0.f;
-            float sv = b0 < P ? open_s[(lv * 2 + 1) * kDH + c] : 0.f;
-            uint64_t mm = chain;
-            while (mm != 0ull) {
-              const int j = __builtin_ctzll(mm);
-              mm &= mm - 1ull;
-              if (P + dep_s[j] >= b0) {
-                sk += bf16_bits_to_f32(*(const uint16_t*)(Ks + (rr + j) * kKStr + c * 2));
-                sv += bf16_bits_to_f32(*(const uint16_t*)(Vr + (rr + j) * kKStr + c * 2));
-              }
-            }
-            if ((pos + 1) % C == 0) {
-              ((uint16_t*)a.scratch.entry_k[lv])[dst] = f32_to_bf16_bits(sk / (float)C);
-              ((uint16_t*)a.scratch.entry_v[lv])[dst] = f32_to_bf16_bits(sv / (float)C);
-              a.scratch.open_k[lv][dst] = 0.f;
-              a.scratch.open_v[lv][dst] = 0.f;
-            } else {
-              a.scratch.open_k[lv][dst] = sk;
-              a.scratch.open_v[lv][dst] = sv;
-            }
-          }
-        }
-      }
       if (wave_has_rows) {
         const uint64_t chain = row < a.R ? anc_s[node] : 0ull;
         const uint64_t vis = (rr > 0 ? (1ull << rr) - 1ull : 0ull) | (rr < 64 ? chain << rr : 0ull);

@@ -153,5 +153,6 @@ hipError_t launch_compress(const tv_state& st, const void* raw_k, const void* ra
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_finish(const AttnArgs& a, hipStream_t s);
+hipError_t launch_scratch(const AttnArgs& a, hipStream_t s);
 
 }  // namespace tv

@@ -56,10 +56,12 @@ tv_status check_state(const tv_state* st) {
                   TV_POOL_ALIGN);
     if (!L.k || !L.vt || !L.n || !L.open_k || !L.open_v)
       return fail(TV_EINVAL, "level %d: NULL pool/count/open-sum pointer", l);
-    if (!aligned16(L.k) || !aligned16(L.vt)) return fail(TV_EINVAL, "level %d: pools must be 16-byte aligned", l);
+    if (!aligned16(L.k) || !aligned16(L.vt) || !aligned16(L.open_k) || !aligned16(L.open_v))
+      return fail(TV_EINVAL, "level %d: pools and open sums must be 16-byte aligned", l);
   }
   if (st->n_levels > 0 && st->lvl[0].C > 1 && (!st->tail_k || !st->tail_v))
     return fail(TV_EINVAL, "tail pointers are NULL");
+  if (!aligned16(st->tail_k) || !aligned16(st->tail_v)) return fail(TV_EINVAL, "tails must be 16-byte aligned");
   return ok();
 }
 
@@ -175,11 +177,16 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
   if (num_parts < 0) return fail(TV_EINVAL, "num_parts = %d < 0", num_parts);
   if (st->B == 0) return ok();
   if (!q || !k_tree || !v_tree || !anc || !depth || !out) return fail(TV_EINVAL, "NULL pointer argument");
-  if (!aligned16(q)) return fail(TV_EINVAL, "q must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+    return fail(TV_EINVAL, "q, k_tree, v_tree and out must be 16-byte aligned");
   if (scratch != nullptr)
-    for (int l = 0; l < st->n_levels; ++l)
+    for (int l = 0; l < st->n_levels; ++l) {
       if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
         return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
+      if (!aligned16(scratch->entry_k[l]) || !aligned16(scratch->entry_v[l]) || !aligned16(scratch->open_k[l]) ||
+          !aligned16(scratch->open_v[l]))
+        return fail(TV_EINVAL, "scratch level %d must be 16-byte aligned", l);
+    }
   const Plan p = make_plan(D, Hq, st, num_parts);
   if (workspace == nullptr || workspace_bytes < p.total)
     return fail(TV_EWORKSPACE, "workspace %zu bytes, need %zu", workspace == nullptr ? (size_t)0 : workspace_bytes,
@@ -212,6 +219,9 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
   const int tree_entries = D + (c0 - 1);
   a.fused_tree = mfma && p.parts > 0 && tree_entries <= 64;
   a.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
+  // the scratch pad needs only the tree tokens, the plan and the committed open sums
+  s = hip_check(tv::launch_scratch(a, stream), "scratch pad launch");
+  if (s != TV_OK) return s;
   if (g_ev_start) {
     s = hip_check(hipEventRecord(g_ev_start, stream), "timing event");
     if (s != TV_OK) return s;
@@ -222,9 +232,9 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
     s = hip_check(hipEventRecord(g_ev_stop, stream), "timing event");
     if (s != TV_OK) return s;
   }
-  // nothing left for the finish kernel when the prefix kernel wrote every row (one
-  // workgroup per unit; it also builds the scratch pad)
-  const bool all_whole = a.fused_tree && p.per == p.tmax && (long long)p.parts == p.units;
+  // nothing left for the finish kernel when every slice is made of whole units: the
+  // prefix kernel then wrote every output row itself
+  const bool all_whole = a.fused_tree && p.per % p.tmax == 0;
   if (all_whole) return ok();
   return hip_check(tv::launch_attn_finish(a, stream), "attention finish launch");
 }
