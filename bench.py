@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--parts", type=int, default=0, help="prefix-stream workgroups (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
+    ap.add_argument("--summarize-profiles", default="", metavar="DIR",
+                    help="write profiles/*.md and the traffic JSON from rocprofv3 csv runs in DIR "
+                         "(kt/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/, kt.txt)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (to scale HBM byte counters)")
     return ap.parse_args()
@@ -60,6 +63,99 @@ def calibrate_copy(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
+
+
+PROFILE_BENCH = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline"
+PROFILE_COUNTER_BENCH = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline"
+PREFIX_KERNEL = "tv::k_attn_mfma"
+
+
+def _counter_per_kernel(path: str, counter: str) -> dict:
+    """Mean counter value (KiB) per dispatch, by kernel name, from a rocprofv3 csv."""
+    import csv
+    acc = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            v = acc.setdefault(r["Kernel_Name"], [0.0, 0])
+            v[0] += float(r["Counter_Value"])
+            v[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
+def summarize_profiles(d: str, workload: str) -> None:
+    """Turn the rocprofv3 csv runs of the profiling commands below into the committed
+    summaries: the kernel-trace statistics, the scaled HBM bytes per dispatch and the
+    traffic record bench.py reports (tagged with the prefix kernel's source digest)."""
+    import csv
+    out_dir = os.path.join(ROOT, "profiles")
+    bench_line = [l for l in open(os.path.join(d, "kt.txt")).read().splitlines() if l.startswith("{")][-1]
+    bl = json.loads(bench_line)
+    kt_cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {PROFILE_BENCH}"
+    rows = list(csv.DictReader(open(os.path.join(d, "kt", "run_kernel_stats.csv"))))
+    ours = [r for r in rows if "tv::" in r["Name"]]
+    total_ns = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# Kernel-trace summary: the verify step at {workload} "
+             f"(B={bl['config']['B']}, D={bl['config']['D']}, {bl['config']['Hq']}/{bl['config']['Hkv']} heads, "
+             f"d={bl['config']['head_dim']}, {bl['dtype']}, {bl['config']['prefix_tokens']}-token prefix)", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", "    " + kt_cmd, "",
+             "Per-kernel statistics (`run_kernel_stats.csv`; calls = warm-up + timed steps).  The bench line of",
+             f"the same run reports the prefix kernel at avg {bl['roofline']['avg_launch_ms'] * 1e3:.1f} us from HIP "
+             f"events on its stream ({bl['roofline']['achieved']:.1f} GB/s).  The profiler slows the kernel; a run",
+             "of the same command without it (`python bench.py`) is the throughput figure.", "",
+             "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in ours:
+        lines.append(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{100.0 * float(r['TotalDurationNs']) / total_ns:.1f}% |")
+    lines += ["", "Bench line of the profiled run:", "", "    " + bench_line, ""]
+    open(os.path.join(out_dir, f"attn_prefix_{workload}_kernel_trace.md"), "w").write("\n".join(lines))
+
+    fetch = _counter_per_kernel(os.path.join(d, "FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_per_kernel(os.path.join(d, "WRITE_SIZE", "run_counter_collection.csv"), "WRITE_SIZE")
+    cf = _counter_per_kernel(os.path.join(d, "copy_FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
+    cw = _counter_per_kernel(os.path.join(d, "copy_WRITE_SIZE", "run_counter_collection.csv"), "WRITE_SIZE")
+    copy_name = [k for k in cf if "copy" in k.lower()][0]
+    copy_bytes = int(json.loads([l for l in open(os.path.join(d, "copy_FETCH_SIZE.txt")).read().splitlines()
+                                 if l.startswith("{")][-1])["calibrate_copy_bytes"])
+    fs = copy_bytes / 1024.0 / cf[copy_name]
+    ws = copy_bytes / 1024.0 / cw[copy_name]
+    pk = [k for k in fetch if PREFIX_KERNEL in k][0]
+    rd = fetch[pk] * 1024.0 * fs
+    wr = write[pk] * 1024.0 * ws
+    alg = bl["roofline"]["algorithmic_bytes_per_launch"]
+    cmd = f"rocprofv3 --pmc {{}} --output-format csv -d <dir> -o run -- {PROFILE_COUNTER_BENCH}"
+    rec = {"kernel": pk, "workload": workload,
+           "command_fetch": cmd.format("FETCH_SIZE"), "command_write": cmd.format("WRITE_SIZE"),
+           "command_calibration": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d <dir> -o run -- "
+                                  "python3 bench.py --calibrate-copy 1024",
+           "fetch_size_kib_per_dispatch": round(fetch[pk], 2), "write_size_kib_per_dispatch": round(write[pk], 2),
+           "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_size_kib": round(cf[copy_name], 2),
+                                "write_size_kib": round(cw[copy_name], 2), "fetch_scale": round(fs, 5),
+                                "write_scale": round(ws, 5)},
+           "hbm_bytes_per_launch": int(rd + wr), "hbm_read_bytes_per_launch": int(rd),
+           "hbm_write_bytes_per_launch": int(wr), "algorithmic_bytes_per_launch": alg,
+           "hbm_over_algorithmic": round((rd + wr) / alg, 4), "kernel_source_digest": kernel_source_digest()}
+    open(os.path.join(out_dir, f"traffic_attn_prefix_{workload}.json"), "w").write(json.dumps(rec, indent=1) + "\n")
+    lines = [f"# HBM bytes per dispatch (FETCH_SIZE, WRITE_SIZE): the verify step at {workload}", "",
+             "Commands (from the repository root, TMPDIR=/tmp), one counter per run:", "",
+             "    " + cmd.format("FETCH_SIZE"), "    " + cmd.format("WRITE_SIZE"),
+             "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python3 bench.py --calibrate-copy 1024",
+             "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- python3 bench.py --calibrate-copy 1024",
+             "", f"Calibration: a {copy_bytes >> 20} MiB device copy reads FETCH_SIZE = {cf[copy_name]:.1f} KiB and "
+             f"WRITE_SIZE = {cw[copy_name]:.1f} KiB per dispatch, so FETCH_SIZE is scaled by {fs:.4f} and "
+             f"WRITE_SIZE by {ws:.4f}.", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |", "|---|---|---|---|---|"]
+    for k in sorted(fetch):
+        if "tv::" not in k:
+            continue
+        lines.append(f"| `{k.split('(')[0].replace('void ', '')}` | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | "
+                     f"{fetch[k] * 1024 * fs / 1e6:.2f} | {write.get(k, 0.0) * 1024 * ws / 1e6:.2f} |")
+    lines += ["", f"Prefix kernel: {(rd + wr) / 1e9:.4f} GB of HBM traffic per launch against {alg / 1e9:.4f} GB "
+              f"algorithmic: ratio {(rd + wr) / alg:.4f}.", ""]
+    open(os.path.join(out_dir, f"hbm_bytes_{workload}.md"), "w").write("\n".join(lines))
+    print(json.dumps(rec))
 
 
 def kernel_source_digest() -> str:
@@ -92,6 +188,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
         return
 
     import torch
