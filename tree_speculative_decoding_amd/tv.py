@@ -270,10 +270,16 @@ def tv_compress_prefix(st, raw_k: torch.Tensor, raw_v: torch.Tensor, seq_err: to
                                     _stream(stream)))
 
 
+def _event_handle(e):
+    """hipEvent_t of a torch.cuda.Event, or an object carrying a raw `handle`."""
+    if e is None:
+        return None
+    h = getattr(e, "handle", None)
+    return ctypes.c_void_p(h if h is not None else e.cuda_event)
+
+
 def tv_set_timing_events(start, stop) -> None:
-    a = ctypes.c_void_p(start.cuda_event) if start is not None else None
-    b = ctypes.c_void_p(stop.cuda_event) if stop is not None else None
-    _check(lib().tv_set_timing_events(a, b))
+    _check(lib().tv_set_timing_events(_event_handle(start), _event_handle(stop)))
 
 
 def tv_version() -> int:
