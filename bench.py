@@ -344,9 +344,41 @@ def main():
         "seq_errors": errs,
         "setup_s": round(setup_s, 1),
     }
+    result["draft_tree"] = time_draft_tree(w, args.steps, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def time_draft_tree(w, steps: int, stream) -> dict:
+    """Device draft-tree construction for the workload's batch and tree shape (top-k,
+    draft steps, budget D; vocabulary w.vocab) from synthetic Gumbel draft logits: the
+    average of `steps` launches, each timed with fence-free HIP events on `stream`."""
+    import torch
+    import tree_speculative_decoding_amd as tv
+    E = sum(w.topk ** l for l in range(w.steps))
+    rng = np.random.default_rng(w.seed + 77)
+    logits = torch.from_numpy(rng.gumbel(size=(w.B, E, w.vocab)).astype(np.float32)).cuda()
+    root = torch.from_numpy(rng.integers(w.vocab, size=w.B).astype(np.int32)).cuda()
+    par = torch.zeros(w.B, w.D, dtype=torch.int32, device="cuda")
+    tok = torch.zeros(w.B, w.D, dtype=torch.int32, device="cuda")
+    tv.tv_build_draft_tree(logits, root, w.topk, w.steps, par, tok, stream=stream)  # warm-up
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    hip = TimingEvent._hip
+    for a_, b_ in ev:
+        hip.hipEventRecord(ctypes_ptr(a_.handle), ctypes_ptr(stream.cuda_stream))
+        tv.tv_build_draft_tree(logits, root, w.topk, w.steps, par, tok, stream=stream)
+        hip.hipEventRecord(ctypes_ptr(b_.handle), ctypes_ptr(stream.cuda_stream))
+    torch.cuda.synchronize()
+    us = float(np.mean([a_.elapsed_ms(b_) for a_, b_ in ev])) * 1e3
+    return {"us_per_launch": round(us, 2), "B": w.B, "topk": w.topk, "draft_steps": w.steps, "D": w.D,
+            "vocab": w.vocab, "logits_bytes": w.B * E * w.vocab * 4,
+            "bound": "latency (one workgroup per sequence; E rows of the vocabulary each)"}
+
+
+def ctypes_ptr(x):
+    import ctypes
+    return ctypes.c_void_p(x)
 
 
 def cpu_baseline(w, budget_s: float):

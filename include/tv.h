@@ -61,6 +61,7 @@ extern "C" {
 #define TV_MAX_LEVELS 2
 #define TV_MAX_D 64
 #define TV_POOL_ALIGN 64    /* every pool capacity must be a multiple of this */
+#define TV_DT_MAX_CAND 2048 /* candidates of an expanded draft tree (tv_build_draft_tree) */
 
 typedef enum {
   TV_OK = 0,
@@ -129,6 +130,29 @@ typedef struct {
  */
 TV_API tv_status tv_build_tree_mask(int B, int D, const int32_t* parents, uint64_t* anc,
                                     int32_t* depth, int32_t* seq_err, hipStream_t stream);
+
+/*
+ * Draft-tree construction (TSD-V4 §2.1: the draft expands the accepted prefix into a
+ * candidate tree, and pruning keeps promising candidates within the verification-token
+ * budget; §4.1 draft extend; §4.3 such metadata prepared on the device).  Expansion:
+ * node e (root = 0, then candidates in creation order) gets the topk tokens with the
+ * largest logits of its row (ties: smaller token id) as children e*topk + 1 ..
+ * e*topk + topk, for `steps` levels, so E = 1 + topk + ... + topk^(steps-1) nodes are
+ * expanded and N = topk + ... + topk^steps candidates created.  A candidate's score is
+ * its parent's plus log_softmax(parent's row)[token] (root: 0), computed in float64.
+ * Pruning keeps the D - 1 best candidates (ties: shallower, then earlier created);
+ * the tree is the root followed by them in rank order, so 0 <= parents[i] < i.
+ *   logits    [B][E][vocab] fp32 in: row e = draft logits after node e (finite or -inf,
+ *             at least one finite value per row)
+ *   root_tok  [B] in: the root's token (the last committed token)
+ *   parents   [B][D] out (parents[b][0] = -1), draft_tok [B][D] out
+ *   cum_logp  [B][D] fp32 out, each node's score (NULL = not wanted)
+ * Limits: topk >= 1, steps >= 1, vocab >= topk, N <= TV_DT_MAX_CAND,
+ * 1 <= D <= min(TV_MAX_D, N + 1).  The output feeds tv_build_tree_mask directly.
+ */
+TV_API tv_status tv_build_draft_tree(int B, int topk, int steps, int D, int vocab, const float* logits,
+                                     const int32_t* root_tok, int32_t* parents, int32_t* draft_tok,
+                                     float* cum_logp, hipStream_t stream);
 
 /*
  * Bytes of device workspace tv_verify_attn needs for this state shape when the

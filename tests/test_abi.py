@@ -110,3 +110,18 @@ def test_status_strings():
     L = tv.lib()
     for code in (0, -1, -2, -3, -4):
         assert L.tv_status_string(code)
+
+
+def test_draft_tree_rejects_bad_sizes():
+    L = tv.lib()
+    f = L.tv_build_draft_tree
+    assert f(2, 0, 3, 8, 1024, P, P, P, P, None, None) == tv.TV_EINVAL       # topk 0
+    assert f(2, 2, 0, 8, 1024, P, P, P, P, None, None) == tv.TV_EINVAL       # steps 0
+    assert f(2, 2, 3, 16, 1024, P, P, P, P, None, None) == tv.TV_EINVAL      # D > N + 1 = 15
+    assert f(2, 2, 3, 0, 1024, P, P, P, P, None, None) == tv.TV_EINVAL       # D 0
+    assert f(2, 4, 3, 65, 1024, P, P, P, P, None, None) == tv.TV_EINVAL      # D > TV_MAX_D
+    assert f(2, 2, 11, 8, 1024, P, P, P, P, None, None) == tv.TV_EINVAL      # N = 4094 > 2048
+    assert b"candidates" in L.tv_last_error()
+    assert f(2, 8, 3, 8, 4, P, P, P, P, None, None) == tv.TV_EINVAL          # vocab < topk
+    assert f(2, 2, 3, 8, 1024, None, P, P, P, None, None) == tv.TV_EINVAL    # NULL logits
+    assert f(0, 2, 3, 8, 1024, None, None, None, None, None, None) == tv.TV_OK  # B = 0

@@ -7,7 +7,7 @@
 // iff its whole chain (its ancestor mask) lies inside that ballot.  A wave max
 // over (depth, -index) picks the path end; every lane on that chain writes its
 // own slot of the path (slots are the distinct depths 0..m).
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

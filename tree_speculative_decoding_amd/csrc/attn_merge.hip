@@ -10,7 +10,7 @@
 // the arithmetic (excluded by selection, not by a -inf score).  Chain scores are
 // reduced eight at a time with interleaved shuffles, then folded into the same
 // base-2 online softmax as the prefix kernels.
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

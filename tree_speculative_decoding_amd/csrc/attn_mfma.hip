@@ -32,7 +32,7 @@
 // workgroup's slice covers the whole unit it normalises and writes the output rows and
 // their LSE; otherwise every workgroup of the unit writes a partial (running max, sum,
 // unnormalised output) for the merge kernel.
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

@@ -10,7 +10,7 @@
 // online-softmax running max (base-2 units), a per-thread partial sum and a quarter
 // of the output row in registers.  The partial (max, sum, unnormalised output) of
 // every unit goes to the workspace for the merge kernel.
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

@@ -8,7 +8,7 @@
 //   raw reads of a block are coalesced; sums in fp32 in position order.
 // k_compress_finish: one workgroup per (sequence, KV head): open-block sums, the
 //   finest level's raw tail, counts and the per-sequence status.
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

@@ -11,7 +11,7 @@
 // path leaf's open-block sums replace the open sums, path tokens extend the raw
 // tail.  Counters (P, n) are written after a barrier, once every thread of the
 // sequence has read the old values.  Rejected nodes are never read.
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

@@ -16,7 +16,7 @@
 // consecutive elements 4t .. 4t+3 of the node's Hkv*d row (per pass of 1024) and walks
 // the node's chain once for every level, issuing the K and V loads of up to eight chain
 // nodes before adding them in chain order.
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

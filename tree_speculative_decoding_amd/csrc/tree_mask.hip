@@ -6,7 +6,7 @@
 // every node is built by pointer jumping over the parent links held in registers:
 // after round r each lane's mask covers its ancestors within distance 2^r - 1, so
 // six rounds cover any tree of <= 64 nodes.  depth = popcount(mask) - 1.
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace tv {
 

@@ -9,7 +9,7 @@
 #include <cstring>
 
 #include "tv.h"
-#include "tv_common.h"
+#include "tv_launch.h"
 
 namespace {
 
@@ -156,6 +156,31 @@ TV_API tv_status tv_build_tree_mask(int B, int D, const int32_t* parents, uint64
   if (B == 0) return ok();
   if (!parents || !anc || !depth || !seq_err) return fail(TV_EINVAL, "NULL pointer argument");
   return hip_check(tv::launch_tree_mask(B, D, parents, anc, depth, seq_err, stream), "tree mask launch");
+}
+
+TV_API tv_status tv_build_draft_tree(int B, int topk, int steps, int D, int vocab, const float* logits,
+                                     const int32_t* root_tok, int32_t* parents, int32_t* draft_tok,
+                                     float* cum_logp, hipStream_t stream) {
+  if (B < 0) return fail(TV_EINVAL, "B = %d < 0", B);
+  if (topk < 1 || steps < 1) return fail(TV_EINVAL, "topk = %d and steps = %d must be >= 1", topk, steps);
+  if (vocab < topk) return fail(TV_EINVAL, "vocab = %d < topk = %d", vocab, topk);
+  // E = 1 + k + ... + k^(steps-1) expanded nodes, N = k + ... + k^steps candidates
+  long long E = 0, N = 0, width = 1;
+  for (int l = 0; l < steps; ++l) {
+    E += width;
+    width *= topk;
+    N += width;
+    if (N > TV_DT_MAX_CAND)
+      return fail(TV_EINVAL, "topk = %d, steps = %d create more than %d candidates", topk, steps, TV_DT_MAX_CAND);
+  }
+  const long long dmax = N + 1 < TV_MAX_D ? N + 1 : TV_MAX_D;
+  if (D < 1 || D > dmax) return fail(TV_EINVAL, "D = %d outside 1..%lld", D, dmax);
+  if ((long long)E * vocab > 0x7fffffffLL) return fail(TV_EINVAL, "E * vocab too large");
+  if (B == 0) return ok();
+  if (!logits || !root_tok || !parents || !draft_tok) return fail(TV_EINVAL, "NULL pointer argument");
+  return hip_check(tv::launch_draft_tree(B, topk, steps, D, vocab, (int)E, (int)N, logits, root_tok, parents,
+                                         draft_tok, cum_logp, stream),
+                   "draft tree launch");
 }
 
 TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_parts) {

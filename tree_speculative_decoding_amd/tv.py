@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
                                   vp, vp, vp, vp], i32),
             "tv_compress_prefix": ([ctypes.POINTER(TvState), vp, vp, i32, vp, vp], i32),
             "tv_set_timing_events": ([vp, vp], i32),
+            "tv_build_draft_tree": ([i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
             "tv_status_string": ([i32], ctypes.c_char_p),
             "tv_last_error": ([], ctypes.c_char_p),
             "tv_version": ([], i32),
@@ -226,6 +227,15 @@ def tv_build_tree_mask(parents: torch.Tensor, anc: torch.Tensor, depth: torch.Te
     B, D = parents.shape
     _check(lib().tv_build_tree_mask(B, D, _ptr(parents), _ptr(anc), _ptr(depth), _ptr(seq_err),
                                     _stream(stream)))
+
+
+def tv_build_draft_tree(logits: torch.Tensor, root_tok: torch.Tensor, topk: int, steps: int,
+                        parents: torch.Tensor, draft_tok: torch.Tensor, cum_logp: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    B, E, V = logits.shape
+    D = parents.shape[1]
+    _check(lib().tv_build_draft_tree(B, topk, steps, D, V, _ptr(logits), _ptr(root_tok), _ptr(parents),
+                                     _ptr(draft_tok), _ptr(cum_logp), _stream(stream)))
 
 
 def tv_verify_attn_workspace_bytes(D: int, Hq: int, st, num_parts: int = 0) -> int:
