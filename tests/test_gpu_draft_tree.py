@@ -54,6 +54,7 @@ CASES = [  # (topk, steps, D, vocab, B)
     (4, 3, 64, 300, 16),     # D = TV_MAX_D
     (16, 2, 64, 100, 8),     # wide: 272 candidates
     (2, 10, 64, 37, 2),      # 2046 candidates, 1023 expanded rows
+    (2, 3, 8, 2000, 16),     # vocabulary past the 1024 kept in registers
 ]
 
 

@@ -14,10 +14,11 @@
 // Scores are kept in float64, so the ranking (an integer result) is not at the mercy of
 // float32 rounding.
 //
-// One workgroup of 256 threads per sequence.  Each wave takes rows e = wave, wave + 4,
+// One workgroup of 512 threads per sequence.  Each wave takes rows e = wave, wave + 8,
 // ...: the row max (wave max), the normaliser sum exp(x - max) in float64 (wave sum), and
 // the top k as k successive wave argmaxes, pick r taking the best token strictly after
-// pick r-1 in the (logit desc, id asc) order, so no chosen set is kept.  Then the scores
+// pick r-1 in the (logit desc, id asc) order, so no chosen set is kept.  A vocabulary of
+// up to 1024 is read once into registers (16 values per lane) for all of these passes.  Then the scores
 // are accumulated level by level in LDS, each candidate's rank is the number of
 // candidates that beat it, and the kept ones are written out.
 #include "tv_launch.h"
@@ -25,7 +26,8 @@
 namespace tv {
 
 namespace {
-constexpr int kDtThreads = 256;
+constexpr int kDtThreads = 512;
+constexpr int kVpl = 16;  // vocabulary entries a lane keeps in registers (vocab <= 1024)
 
 // (v, t) comes before (bv, bt) in the order logits descending, ids ascending
 __device__ __forceinline__ bool before(float v, int t, float bv, int bt) {
@@ -46,14 +48,32 @@ __global__ __launch_bounds__(kDtThreads) void k_draft_tree(int k, int steps, int
   const float* lg = logits + (size_t)b * E * V;
 
   // 1. per expanded row: normaliser and top k
+  const bool cached = V <= 64 * kVpl;  // uniform
   for (int e = w; e < E; e += kDtThreads / 64) {
     const float* row = lg + (size_t)e * V;
+    float xv[kVpl];
     float m = -INFINITY;
-    for (int t = lane; t < V; t += 64) m = fmaxf(m, row[t]);
+    if (cached) {
+#pragma unroll
+      for (int i = 0; i < kVpl; ++i) {
+        const int t = lane + 64 * i;
+        xv[i] = t < V ? row[t] : -INFINITY;
+        m = fmaxf(m, xv[i]);
+      }
+    } else {
+      for (int t = lane; t < V; t += 64) m = fmaxf(m, row[t]);
+    }
     m = wave_max(m);
     double s = 0.0;
-    if (m != -INFINITY)
-      for (int t = lane; t < V; t += 64) s += exp((double)row[t] - (double)m);
+    if (m != -INFINITY) {
+      if (cached) {
+#pragma unroll
+        for (int i = 0; i < kVpl; ++i)
+          if (lane + 64 * i < V) s += exp((double)xv[i] - (double)m);
+      } else {
+        for (int t = lane; t < V; t += 64) s += exp((double)row[t] - (double)m);
+      }
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
     const double lse = m == -INFINITY ? -INFINITY : (double)m + log(s);
@@ -62,11 +82,22 @@ __global__ __launch_bounds__(kDtThreads) void k_draft_tree(int k, int steps, int
     for (int r = 0; r < k; ++r) {
       float bv = -INFINITY;
       int bt = 0x7fffffff;
-      for (int t = lane; t < V; t += 64) {
-        const float v = row[t];
-        if (before(pv, pt, v, t) && before(v, t, bv, bt)) {
-          bv = v;
-          bt = t;
+      if (cached) {
+#pragma unroll
+        for (int i = 0; i < kVpl; ++i) {
+          const int t = lane + 64 * i;
+          if (t < V && before(pv, pt, xv[i], t) && before(xv[i], t, bv, bt)) {
+            bv = xv[i];
+            bt = t;
+          }
+        }
+      } else {
+        for (int t = lane; t < V; t += 64) {
+          const float v = row[t];
+          if (before(pv, pt, v, t) && before(v, t, bv, bt)) {
+            bv = v;
+            bt = t;
+          }
         }
       }
 #pragma unroll
