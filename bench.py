@@ -345,6 +345,7 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     result["draft_tree"] = time_draft_tree(w, args.steps, stream)
+    result["draft_attn"] = time_draft_attn(w, st, stream, reps=3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -374,6 +375,57 @@ def time_draft_tree(w, steps: int, stream) -> dict:
     return {"us_per_launch": round(us, 2), "B": w.B, "topk": w.topk, "draft_steps": w.steps, "D": w.D,
             "vocab": w.vocab, "logits_bytes": w.B * E * w.vocab * 4,
             "bound": "latency (one workgroup per sequence; E rows of the vocabulary each)"}
+
+
+def time_draft_attn(w, st, stream, reps: int) -> dict:
+    """Draft-decode reuse of the branch-aware attention: for each level t of the
+    workload's expansion (top-k, draft steps), tv_draft_attn over the 1 + k + ... +
+    k^(t-1) nodes created so far, with one plan of the whole expansion shared by the
+    levels; each launch is timed with fence-free events on `stream` (`reps` per level).
+    Synthetic Q / tree K/V of the workload's dtype; the state is the benchmark's."""
+    import torch
+    import synth
+    import tree_speculative_decoding_amd as tv
+    k, s = w.topk, w.steps
+    n = sum(k ** l for l in range(s + 1))
+    rng = np.random.default_rng(w.seed + 78)
+    par = np.array([-1] + [(c - 1) // k for c in range(1, n)], dtype=np.int32)
+    parents = torch.from_numpy(np.tile(par, (w.B, 1))).cuda()
+
+    def vals(shape):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        return tv.to_device(synth.f32_to_bf16_bits(x) if w.dtype == "bf16" else x, w.dtype)
+
+    q, kt, vt = vals((w.B, n, w.Hq, w.d)), vals((w.B, n, w.Hkv, w.d)), vals((w.B, n, w.Hkv, w.d))
+    anc = torch.zeros(w.B, n, dtype=torch.int64, device="cuda")
+    depth = torch.zeros(w.B, n, dtype=torch.int32, device="cuda")
+    err = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    tv.tv_build_tree_mask(parents, anc, depth, err, stream)
+    e = 2 if w.dtype == "bf16" else 4
+    entries = sum(int(x.sum()) for x in st.n) / w.B
+    tail = float((st.P % w.levels[0]).float().mean().item()) if w.levels[0] > 1 else 0.0
+    levels, us, frac = [], [], []
+    for t in range(1, s + 1):
+        D = sum(k ** l for l in range(t))
+        qd, kd, vd = q[:, :D].contiguous(), kt[:, :D].contiguous(), vt[:, :D].contiguous()
+        out = torch.empty(w.B, D, w.Hq, w.d, dtype=qd.dtype, device="cuda")
+        ws = torch.empty(tv.tv_verify_attn_workspace_bytes(D, w.Hq, st) // 4 + 64, dtype=torch.float32,
+                         device="cuda")
+        tv.tv_draft_attn(qd, kd, vd, anc, err, st, out, None, ws, stream=stream)  # warm-up
+        ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
+        for a_, b_ in ev:
+            tv.tv_set_timing_events(a_, b_)
+            tv.tv_draft_attn(qd, kd, vd, anc, err, st, out, None, ws, stream=stream)
+        tv.tv_set_timing_events(None, None)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a_.elapsed_ms(b_) for a_, b_ in ev]))
+        nbytes = w.B * (w.Hkv * (entries + tail) * w.d * 2 * e + D * w.Hq * w.d * 2 * e + D * w.Hkv * w.d * 2 * e
+                        + 8 * D)
+        levels.append(D)
+        us.append(round(ms * 1e3, 1))
+        frac.append(round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+    return {"nodes_per_level": levels, "us_per_launch": us, "hbm_frac": frac, "expansion_nodes": n,
+            "note": "same prefix stream as verify; rows for every node created so far"}
 
 
 def ctypes_ptr(x):

@@ -192,6 +192,25 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
                                 hipStream_t stream);
 
 /*
+ * Branch-aware attention of one draft-decode level (TSD-V4 §4.1: draft decode computes
+ * the candidates' representations under the tree topology; §4.3: the same metadata
+ * serves draft and verify).  The candidate tree grows level by level in creation order
+ * (parents before children), so the nodes created so far are the first D nodes and
+ * their plan is the first D entries of each row of the whole expansion's plan: anc is
+ * [B][anc_ld] from one tv_build_tree_mask call over all anc_ld nodes, shared by every
+ * level.  Rows are computed for all D nodes with the same visibility as
+ * tv_verify_attn (no scratch pad); a node's row depends only on its own chain, so the
+ * rows of earlier levels are what those levels produced.
+ *   q [B][D][Hq][d], k_tree, v_tree [B][D][Hkv][d], out [B][D][Hq][d], lse [B][D][Hq]
+ *   workspace: >= tv_verify_attn_workspace_bytes(D, Hq, st, num_parts) bytes
+ * 1 <= D <= anc_ld <= TV_MAX_D.
+ */
+TV_API tv_status tv_draft_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
+                               const void* v_tree, const uint64_t* anc, const int32_t* seq_err,
+                               const tv_state* st, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, int num_parts, hipStream_t stream);
+
+/*
  * Accepted-path selection (TSD-V4 §3.1: the result is a specific path through the
  * tree; §4.4 accepted-path selection).  Greedy rule: draft node i >= 1 is correct
  * iff draft_tok[i] == target_tok[parent(i)] (target_tok[u] = the target model's

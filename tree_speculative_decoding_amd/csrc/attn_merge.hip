@@ -101,7 +101,7 @@ __global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
     }
 
     // the node's own chain (ancestors and itself), eight nodes per round
-    uint64_t chain = a.fused_tree ? 0ull : a.anc[(size_t)b * a.D + i] & nodes;
+    uint64_t chain = a.fused_tree ? 0ull : a.anc[(size_t)b * a.anc_ld + i] & nodes;
     while (chain != 0ull) {
       int nj[8];
       float sc[8];

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
         }
       }
       if (tid < a.D) {
-        anc_j = a.anc[(size_t)b * a.D + tid];
+        anc_j = a.anc[(size_t)b * a.anc_ld + tid];
       }
     }
 

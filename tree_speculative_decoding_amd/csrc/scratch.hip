@@ -49,12 +49,12 @@ __global__ __launch_bounds__(256) void k_scratch(AttnArgs a) {
   const int b = blockIdx.x / a.D;
   const int i = blockIdx.x - b * a.D;
   const int tid = threadIdx.x;
-  if (tid < a.D) dep_s[tid] = a.depth[(size_t)b * a.D + tid];
+  if (tid < a.D) dep_s[tid] = a.depth[(size_t)b * a.anc_ld + tid];
   __syncthreads();
   if (a.seq_err != nullptr && a.seq_err[b] != TV_SEQ_OK) return;  // uniform
 
   const int P = a.P[b];
-  const uint64_t chain = a.anc[(size_t)b * a.D + i] & node_mask(a.D);
+  const uint64_t chain = a.anc[(size_t)b * a.anc_ld + i] & node_mask(a.D);
   const int pos = P + dep_s[i];
   int b0[TV_MAX_LEVELS];
 #pragma unroll

@@ -88,8 +88,9 @@ struct AttnArgs {
   const void* q;
   const void* k_tree;
   const void* v_tree;
-  const uint64_t* anc;
-  const int32_t* depth;
+  const uint64_t* anc;                // [B][anc_ld]: the first D entries of a row are this tree's
+  const int32_t* depth;               // [B][anc_ld]
+  int anc_ld;                         // row length of anc and depth (>= D)
   const int32_t* seq_err;            // may be null
   void* out;
   float* lse;                        // may be null

@@ -123,6 +123,84 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   return p;
 }
 
+// Branch-aware attention of D tree nodes (verify, or one draft-decode level); anc and
+// depth rows are anc_ld long (the tree's first D nodes are the ones attended here).
+tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree, const void* v_tree,
+                   const uint64_t* anc, const int32_t* depth, const int32_t* seq_err, const tv_state* st,
+                   const tv_scratch* scratch, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   int num_parts, hipStream_t stream) {
+  tv_status s = check_state(st);
+  if (s != TV_OK) return s;
+  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
+  if (anc_ld < D || anc_ld > TV_MAX_D) return fail(TV_EINVAL, "anc_ld = %d outside D..%d", anc_ld, TV_MAX_D);
+  if (Hq < 1 || Hq % st->Hkv != 0) return fail(TV_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, st->Hkv);
+  if (num_parts < 0) return fail(TV_EINVAL, "num_parts = %d < 0", num_parts);
+  if (st->B == 0) return ok();
+  if (!q || !k_tree || !v_tree || !anc || !out) return fail(TV_EINVAL, "NULL pointer argument");
+  if (scratch != nullptr && !depth) return fail(TV_EINVAL, "the scratch pad needs depth");
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
+    return fail(TV_EINVAL, "q, k_tree, v_tree and out must be 16-byte aligned");
+  if (scratch != nullptr)
+    for (int l = 0; l < st->n_levels; ++l) {
+      if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
+        return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
+      if (!aligned16(scratch->entry_k[l]) || !aligned16(scratch->entry_v[l]) || !aligned16(scratch->open_k[l]) ||
+          !aligned16(scratch->open_v[l]))
+        return fail(TV_EINVAL, "scratch level %d must be 16-byte aligned", l);
+    }
+  const Plan p = make_plan(D, Hq, st, num_parts);
+  if (workspace == nullptr || workspace_bytes < p.total)
+    return fail(TV_EWORKSPACE, "workspace %zu bytes, need %zu", workspace == nullptr ? (size_t)0 : workspace_bytes,
+                p.total);
+  if (!aligned16(workspace)) return fail(TV_EINVAL, "workspace must be 16-byte aligned");
+
+  tv::AttnArgs a{};
+  a.B = st->B; a.D = D; a.Hq = Hq; a.Hkv = st->Hkv; a.d = st->d; a.G = Hq / st->Hkv; a.R = p.R;
+  a.dtype = st->dtype; a.n_levels = st->n_levels;
+  for (int l = 0; l < st->n_levels; ++l) {
+    a.C[l] = st->lvl[l].C; a.cap[l] = st->lvl[l].cap;
+    a.pk[l] = st->lvl[l].k; a.pvt[l] = st->lvl[l].vt; a.pn[l] = st->lvl[l].n;
+    a.open_k[l] = st->lvl[l].open_k; a.open_v[l] = st->lvl[l].open_v;
+  }
+  a.tail_k = st->tail_k; a.tail_v = st->tail_v; a.P = st->P;
+  a.anc_ld = anc_ld;
+  a.q = q; a.k_tree = k_tree; a.v_tree = v_tree; a.anc = anc; a.depth = depth; a.seq_err = seq_err;
+  a.out = out; a.lse = lse;
+  if (scratch != nullptr) a.scratch = *scratch;
+  a.build_scratch = scratch != nullptr;
+  a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
+  a.smax = p.smax;
+  const int c0 = st->n_levels > 0 ? st->lvl[0].C : 1;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
+  a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);
+
+  const bool mfma = st->dtype == TV_BF16 && st->d == 128;
+  // the tail (< C0 tokens) and the D tree tokens form one extra chunk of at most 64
+  // entries, attended in 16-entry tiles
+  const int tree_entries = D + (c0 - 1);
+  a.fused_tree = mfma && p.parts > 0 && tree_entries <= 64;
+  a.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
+  // the scratch pad needs only the tree tokens, the plan and the committed open sums
+  s = hip_check(tv::launch_scratch(a, stream), "scratch pad launch");
+  if (s != TV_OK) return s;
+  if (g_ev_start) {
+    s = hip_check(hipEventRecord(g_ev_start, stream), "timing event");
+    if (s != TV_OK) return s;
+  }
+  s = hip_check(mfma ? tv::launch_attn_mfma(a, stream) : tv::launch_attn_valu(a, stream), "prefix attention launch");
+  if (s != TV_OK) return s;
+  if (g_ev_stop) {
+    s = hip_check(hipEventRecord(g_ev_stop, stream), "timing event");
+    if (s != TV_OK) return s;
+  }
+  // nothing left for the finish kernel when every slice is made of whole units: the
+  // prefix kernel then wrote every output row itself
+  const bool all_whole = a.fused_tree && p.per % p.tmax == 0;
+  if (all_whole) return ok();
+  return hip_check(tv::launch_attn_finish(a, stream), "attention finish launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,73 +273,17 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
                                 const tv_state* st, const tv_scratch* scratch, void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, int num_parts,
                                 hipStream_t stream) {
-  tv_status s = check_state(st);
-  if (s != TV_OK) return s;
-  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
-  if (Hq < 1 || Hq % st->Hkv != 0) return fail(TV_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, st->Hkv);
-  if (num_parts < 0) return fail(TV_EINVAL, "num_parts = %d < 0", num_parts);
-  if (st->B == 0) return ok();
-  if (!q || !k_tree || !v_tree || !anc || !depth || !out) return fail(TV_EINVAL, "NULL pointer argument");
-  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
-    return fail(TV_EINVAL, "q, k_tree, v_tree and out must be 16-byte aligned");
-  if (scratch != nullptr)
-    for (int l = 0; l < st->n_levels; ++l) {
-      if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
-        return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
-      if (!aligned16(scratch->entry_k[l]) || !aligned16(scratch->entry_v[l]) || !aligned16(scratch->open_k[l]) ||
-          !aligned16(scratch->open_v[l]))
-        return fail(TV_EINVAL, "scratch level %d must be 16-byte aligned", l);
-    }
-  const Plan p = make_plan(D, Hq, st, num_parts);
-  if (workspace == nullptr || workspace_bytes < p.total)
-    return fail(TV_EWORKSPACE, "workspace %zu bytes, need %zu", workspace == nullptr ? (size_t)0 : workspace_bytes,
-                p.total);
-  if (!aligned16(workspace)) return fail(TV_EINVAL, "workspace must be 16-byte aligned");
+  if (depth == nullptr && st != nullptr && st->B > 0) return fail(TV_EINVAL, "NULL pointer argument (depth)");
+  return run_attn(D, D, Hq, q, k_tree, v_tree, anc, depth, seq_err, st, scratch, out, lse, workspace,
+                  workspace_bytes, num_parts, stream);
+}
 
-  tv::AttnArgs a{};
-  a.B = st->B; a.D = D; a.Hq = Hq; a.Hkv = st->Hkv; a.d = st->d; a.G = Hq / st->Hkv; a.R = p.R;
-  a.dtype = st->dtype; a.n_levels = st->n_levels;
-  for (int l = 0; l < st->n_levels; ++l) {
-    a.C[l] = st->lvl[l].C; a.cap[l] = st->lvl[l].cap;
-    a.pk[l] = st->lvl[l].k; a.pvt[l] = st->lvl[l].vt; a.pn[l] = st->lvl[l].n;
-    a.open_k[l] = st->lvl[l].open_k; a.open_v[l] = st->lvl[l].open_v;
-  }
-  a.tail_k = st->tail_k; a.tail_v = st->tail_v; a.P = st->P;
-  a.q = q; a.k_tree = k_tree; a.v_tree = v_tree; a.anc = anc; a.depth = depth; a.seq_err = seq_err;
-  a.out = out; a.lse = lse;
-  if (scratch != nullptr) a.scratch = *scratch;
-  a.build_scratch = scratch != nullptr;
-  a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
-  a.smax = p.smax;
-  const int c0 = st->n_levels > 0 ? st->lvl[0].C : 1;
-  a.ws_o = (float*)workspace;
-  a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
-  a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);
-
-  const bool mfma = st->dtype == TV_BF16 && st->d == 128;
-  // the tail (< C0 tokens) and the D tree tokens form one extra chunk of at most 64
-  // entries, attended in 16-entry tiles
-  const int tree_entries = D + (c0 - 1);
-  a.fused_tree = mfma && p.parts > 0 && tree_entries <= 64;
-  a.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
-  // the scratch pad needs only the tree tokens, the plan and the committed open sums
-  s = hip_check(tv::launch_scratch(a, stream), "scratch pad launch");
-  if (s != TV_OK) return s;
-  if (g_ev_start) {
-    s = hip_check(hipEventRecord(g_ev_start, stream), "timing event");
-    if (s != TV_OK) return s;
-  }
-  s = hip_check(mfma ? tv::launch_attn_mfma(a, stream) : tv::launch_attn_valu(a, stream), "prefix attention launch");
-  if (s != TV_OK) return s;
-  if (g_ev_stop) {
-    s = hip_check(hipEventRecord(g_ev_stop, stream), "timing event");
-    if (s != TV_OK) return s;
-  }
-  // nothing left for the finish kernel when every slice is made of whole units: the
-  // prefix kernel then wrote every output row itself
-  const bool all_whole = a.fused_tree && p.per % p.tmax == 0;
-  if (all_whole) return ok();
-  return hip_check(tv::launch_attn_finish(a, stream), "attention finish launch");
+TV_API tv_status tv_draft_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree, const void* v_tree,
+                               const uint64_t* anc, const int32_t* seq_err, const tv_state* st, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes, int num_parts,
+                               hipStream_t stream) {
+  return run_attn(D, anc_ld, Hq, q, k_tree, v_tree, anc, nullptr, seq_err, st, nullptr, out, lse, workspace,
+                  workspace_bytes, num_parts, stream);
 }
 
 TV_API tv_status tv_accept(int B, int D, const int32_t* parents, const uint64_t* anc, const int32_t* depth,

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
             "tv_compress_prefix": ([ctypes.POINTER(TvState), vp, vp, i32, vp, vp], i32),
             "tv_set_timing_events": ([vp, vp], i32),
             "tv_build_draft_tree": ([i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+            "tv_draft_attn": ([i32, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(TvState), vp, vp, vp, sz, i32,
+                               vp], i32),
             "tv_status_string": ([i32], ctypes.c_char_p),
             "tv_last_error": ([], ctypes.c_char_p),
             "tv_version": ([], i32),
@@ -255,6 +257,19 @@ def tv_verify_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, 
                                 ctypes.byref(sc) if sc is not None else None, _ptr(out), _ptr(lse),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 num_parts, _stream(stream)))
+
+
+def tv_draft_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, anc: torch.Tensor,
+                  seq_err: Optional[torch.Tensor], st, out: torch.Tensor, lse: Optional[torch.Tensor],
+                  workspace: torch.Tensor, num_parts: int = 0, stream=None) -> None:
+    """One draft-decode level: q, k_tree, v_tree, out cover the D nodes created so far;
+    anc is the [B][anc_ld] plan of the whole expansion."""
+    B, D, Hq, d = q.shape
+    anc_ld = anc.shape[1]
+    s = _state(st)
+    _check(lib().tv_draft_attn(D, anc_ld, Hq, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(anc), _ptr(seq_err),
+                               ctypes.byref(s), _ptr(out), _ptr(lse), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), num_parts, _stream(stream)))
 
 
 def tv_accept(parents, anc, depth, draft_tok, target_tok, seq_err, m, path, bonus, stream=None) -> None:
