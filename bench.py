@@ -246,10 +246,8 @@ def main():
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
         for b, lv in enumerate(ex.map(draw, range(B))):
             for l, (k, vt) in enumerate(lv):
-                n = k.shape[1]
-                st.pool_k[l][b, :, :n] = tv.to_device(k, w.dtype)
-                st.pool_vt[l][b] = tv.to_device(vt, w.dtype)
-                st.n[l][b] = n
+                st.write_seq(l, b, tv.to_device(k, w.dtype), tv.to_device(vt, w.dtype))
+                st.n[l][b] = k.shape[1]
     st.P.fill_(w.P)
 
     # ---- per-step inputs (N_INPUT_SETS sets, rotated)

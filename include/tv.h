@@ -57,7 +57,7 @@ extern "C" {
 #define TV_API
 #endif
 
-#define TV_VERSION 100      /* 1.0.0 */
+#define TV_VERSION 110      /* 1.1.0 */
 #define TV_MAX_LEVELS 2
 #define TV_MAX_D 64
 #define TV_POOL_ALIGN 64    /* every pool capacity must be a multiple of this */
@@ -79,20 +79,32 @@ enum {
   TV_SEQ_BAD_PARENT = 1,  /* parents[b] is not a topologically ordered tree */
   TV_SEQ_POOL_FULL = 2,   /* committing would exceed a pool's capacity */
   TV_SEQ_BAD_PREFIX = 3,  /* tv_compress_prefix: P[b] outside [0, max_len] */
-  TV_SEQ_BAD_PATH = 4     /* tv_refresh_state: m or a path node out of range, or P < 0 */
+  TV_SEQ_BAD_PATH = 4,    /* tv_refresh_state: m or a path node out of range, or P < 0 */
+  TV_SEQ_BAD_PAGE = 5     /* a page-table entry needed for a write is outside [0, num_pages) */
 };
 
-/* One compression level (the pages' C4 / C128 compressed states, TSD-V4 §2.2, §4.3). */
+/* One compression level (the pages' C4 / C128 compressed states, TSD-V4 §2.2, §4.3).
+ * A level's entries live in 64-entry tiles (TV_POOL_ALIGN): tile t of (sequence b, KV
+ * head g) holds entries 64t .. 64t+63, as 64 rows of d (K) and as d rows of 64 (V,
+ * transposed inside the tile).  Contiguous pool (page_table == NULL): tile t of (b, g) is
+ * tile (b*Hkv + g)*cap/64 + t of k and vt.  Paged pool (TSD-V4 §4.2: a page-based pool
+ * whose pages are referenced by pointers): k and vt hold num_pages physical pages, each
+ * the tiles of all Hkv heads for 64 entries ([num_pages][Hkv][64][d] and
+ * [num_pages][Hkv][d][64]); page_table[b][t] is the physical page of sequence b's
+ * entries 64t .. 64t+63, and cap = 64 * pages_per_seq.  Page ids outside
+ * [0, num_pages) are never dereferenced: attention reads zeros for them, refresh and
+ * compression flag the sequence TV_SEQ_BAD_PAGE. */
 typedef struct {
   int32_t C;        /* block size: tokens per compressed entry (>= 1) */
-  int32_t cap;      /* pool capacity in entries, a multiple of TV_POOL_ALIGN */
-  void* k;          /* [B][Hkv][cap][d]  committed entries, row-major (entry-major) */
-  void* vt;         /* [B][Hkv][cap/64][d][64] committed entries, transposed within each aligned
-                       block of 64 entries (entry j, channel c at [j/64][c][j%64]): a block of
-                       64 entries is one contiguous 64*d-element tile */
+  int32_t cap;      /* capacity in entries, a multiple of TV_POOL_ALIGN */
+  void* k;          /* contiguous: [B][Hkv][cap][d]; paged: [num_pages][Hkv][64][d] */
+  void* vt;         /* contiguous: [B][Hkv][cap/64][d][64]; paged: [num_pages][Hkv][d][64] */
   int32_t* n;       /* [B] committed entries of each sequence (kept equal to P/C) */
   float* open_k;    /* [B][Hkv][d] fp32 sum of the committed tokens of the open block */
   float* open_v;    /* [B][Hkv][d] */
+  int32_t* page_table;     /* [B][pages_per_seq], or NULL for a contiguous pool */
+  int32_t pages_per_seq;   /* paged: cap / 64 */
+  int32_t num_pages;       /* paged: physical pages in k and vt */
 } tv_level;
 
 /* Persistent compressed state of B sequences (TSD-V4 §4.2 "persistent context"). */

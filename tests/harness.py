@@ -69,12 +69,14 @@ def oracle_state(w: synth.Workload, caps: List[int], batch: Optional[List[int]] 
 
 # ----------------------------------------------------------------------------- device side
 
-def device_state(w: synth.Workload, caps: List[int], poison: bool = False):
+def device_state(w: synth.Workload, caps: List[int], poison: bool = False, page_seed: Optional[int] = None,
+                 spare_pages: int = 0):
     """Device state of workload w at step 0.  With poison=True every pool slot beyond the
-    committed entries holds NaN (they must never be read)."""
+    committed entries holds NaN (they must never be read).  page_seed: a paged pool with a
+    random page table (and spare_pages unused pages, poisoned too)."""
     import torch
     import tree_speculative_decoding_amd as tv
-    st = tv.DeviceState(w.B, w.Hkv, w.d, w.dtype, w.levels, caps)
+    st = tv.DeviceState(w.B, w.Hkv, w.d, w.dtype, w.levels, caps, page_seed=page_seed, spare_pages=spare_pages)
     if poison:
         for t in st.pool_k + st.pool_vt:
             t.fill_(float("nan"))
@@ -95,10 +97,8 @@ def device_state(w: synth.Workload, caps: List[int], poison: bool = False):
     with cf.ThreadPoolExecutor(max_workers=8) as ex:
         for b, lv in enumerate(ex.map(draw, range(w.B))):
             for l, (k, vt) in enumerate(lv):
-                n = k.shape[1]
-                st.pool_k[l][b, :, :n] = tv.to_device(k, w.dtype)
-                st.pool_vt[l][b] = tv.to_device(vt, w.dtype)
-                st.n[l][b] = n
+                st.write_seq(l, b, tv.to_device(k, w.dtype), tv.to_device(vt, w.dtype))
+                st.n[l][b] = k.shape[1]
     st.P.fill_(w.P)
     torch.cuda.synchronize()
     return st
@@ -220,8 +220,8 @@ def compare_state(dst, ost: oracle.State, dtype: str, what: str = "", batch: Opt
             lo = 0 if first_entry is None else int(first_entry[l][k])
             rk = ost.pool_k[l][k, :, lo:nb]
             rv = ost.pool_v[l][k, :, lo:nb]
-            gk = host_f64(dst.pool_k[l][b, :, lo:nb].contiguous(), dtype)
-            gv = tv.tv.untile_vt(host_f64(dst.pool_vt[l][b], dtype))[:, lo:nb]
+            gk = host_f64(dst.logical_k(l)[b, :, lo:nb].contiguous(), dtype)
+            gv = tv.tv.untile_vt(host_f64(dst.logical_vt(l)[b].contiguous(), dtype))[:, lo:nb]
             assert (np.abs(gk - rk) <= entry_tol(dtype, rk)).all(), f"{what} level {l} seq {b} K entries"
             assert (np.abs(gv - rv) <= entry_tol(dtype, rv)).all(), f"{what} level {l} seq {b} V entries"
         ok_ = dst.open_k[l].cpu().numpy().astype(np.float64)[bs]

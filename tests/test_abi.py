@@ -15,14 +15,15 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert tv.tv_version() == 100
+    assert tv.tv_version() == 110
 
 
 def test_struct_layout_matches_header():
-    # tv_level: 2 x int32 + 5 pointers; tv_state: 5 x int32, 2 levels, 3 pointers
-    assert ctypes.sizeof(tv.tv.TvLevel) == 48
-    assert ctypes.sizeof(TvState) == 144
-    assert TvState.lvl.offset == 24 and TvState.P.offset == 136
+    # tv_level: 2 x int32 + 6 pointers + 2 x int32; tv_state: 5 x int32, 2 levels, 3 pointers
+    assert ctypes.sizeof(tv.tv.TvLevel) == 64
+    assert tv.tv.TvLevel.page_table.offset == 48 and tv.tv.TvLevel.num_pages.offset == 60
+    assert ctypes.sizeof(TvState) == 176
+    assert TvState.lvl.offset == 24 and TvState.P.offset == 168
     assert ctypes.sizeof(TvScratch) == 64
 
 

@@ -1,0 +1,168 @@
+"""Paged compressed-KV pools (TSD-V4 §4.2: a page-based pool whose pages are referenced by
+pointers): every 64-entry tile of a sequence lives in a physical page named by a page
+table (random permutations here, with spare pages poisoned).  Verify, draft attention,
+compression and multi-step refresh on a paged state give bit-identical results to the
+same run on a contiguous state (same arithmetic, same chunk order) and match the oracle;
+a missing page is never dereferenced and flags the sequence."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from harness import (Runner, check_attention, compare_state, device_state, host_f64, oracle_state, pooled_caps,
+                     upload_step, widen_step)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _equal(a, b):
+    import torch
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+VERIFY = {
+    "linear_bf16": (synth.WORKLOADS["linear"], 0),
+    "tree_bf16_split": (synth.WORKLOADS["tree"], 7),        # units split over slices: merge kernel
+    "bf16_ragged": (synth.Workload("pg1", 3, 5, 40, 8, 128, "bf16", (4, 128), 4733, 2, 3, 0.6, 4001, prefix="raw"), 0),
+    "f32_d64": (synth.Workload("pg2", 2, 8, 8, 2, 64, "f32", (4, 16), 603, 2, 3, 0.6, 4002, prefix="raw"), 0),
+}
+
+
+@pytest.mark.parametrize("name", list(VERIFY))
+def test_verify_paged_equals_contiguous(name):
+    import torch
+    w, parts = VERIFY[name]
+    _say(f"paged verify {name}")
+    caps = pooled_caps(w, 64)
+    s = synth.step_inputs(w, 0)
+    outs = []
+    for page_seed in (None, 11):
+        dst = device_state(w, caps, poison=True, page_seed=page_seed, spare_pages=5)
+        x = upload_step(s, w.dtype)
+        r = Runner(dst, w.D, w.Hq, parts)
+        r.plan(x)
+        r.attend(x)
+        torch.cuda.synchronize()
+        outs.append((r.out.clone(), r.lse.clone(), [t.clone() for t in r.sc.entry_k + r.sc.open_k]))
+    (o1, l1, s1), (o2, l2, s2) = outs
+    assert _equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(s1, s2):
+        assert _equal(a, b)
+    # and the oracle
+    ost = oracle_state(w, caps)
+    h = widen_step(s, w.dtype)
+    anc, depth, err = oracle.build_plan(s.parents)
+    ref, _ = oracle.verify_attention(h.q, h.kt, h.vt, anc, ost, err)
+    check_attention(host_f64(o2, w.dtype), ref, w.dtype)
+
+
+def test_multistep_paged_against_oracle_and_contiguous():
+    import torch
+    w = synth.Workload("pg3", 3, 8, 16, 2, 128, "bf16", (4, 128), 125, 2, 3, 0.8, 4003, prefix="raw")
+    T = 40
+    _say(f"paged multistep: {T} steps")
+    caps = pooled_caps(w, T * w.D + 8)
+    dst_c = device_state(w, caps, poison=True)
+    dst_p = device_state(w, caps, poison=True, page_seed=5, spare_pages=3)
+    ost = oracle_state(w, caps)
+    rc, rp = Runner(dst_c, w.D, w.Hq), Runner(dst_p, w.D, w.Hq)
+    for t in range(T):
+        s = synth.step_inputs(w, t)
+        h = widen_step(s, w.dtype)
+        xc, xp = upload_step(s, w.dtype), upload_step(s, w.dtype)
+        rc.step(xc)
+        rp.step(xp)
+        torch.cuda.synchronize()
+        assert _equal(rc.out, rp.out), f"step {t} output"
+        assert (rc.log.cpu().numpy() == rp.log.cpu().numpy()).all()
+        ref = oracle.step(ost, s.parents, s.draft, s.target, h.q, h.kt, h.vt)
+        assert (rp.m.cpu().numpy() == ref.m).all() and (rp.err.cpu().numpy() == ref.err).all()
+        ost = ref.state
+        compare_state(dst_p, ost, w.dtype, f"paged step {t}")
+    for l in range(len(w.levels)):
+        n = dst_c.n[l].cpu().numpy()
+        kc, kp = dst_c.logical_k(l), dst_p.logical_k(l)
+        vc, vp = dst_c.logical_vt(l), dst_p.logical_vt(l)
+        for b in range(w.B):
+            assert _equal(kc[b, :, :n[b]], kp[b, :, :n[b]])
+            tiles = (int(n[b]) + 63) // 64
+            full = int(n[b]) // 64
+            assert _equal(vc[b, :, :full], vp[b, :, :full])
+            if tiles > full:  # the partial last tile: committed entries only
+                r = int(n[b]) % 64
+                assert _equal(vc[b, :, full, :, :r], vp[b, :, full, :, :r])
+
+
+def test_draft_attention_paged():
+    import torch
+    import tree_speculative_decoding_amd as tv
+    w = synth.Workload("pg4", 2, 15, 16, 2, 128, "bf16", (4, 128), 900, 2, 3, 0.6, 4004, prefix="raw")
+    _say("paged draft attention")
+    caps = pooled_caps(w, 64)
+    k, s_ = 2, 3
+    n = 15
+    rng = np.random.default_rng(3)
+    par = np.tile(np.array([-1] + [(c - 1) // k for c in range(1, n)], dtype=np.int32), (w.B, 1))
+    vals = lambda shape: synth.f32_to_bf16_bits(rng.standard_normal(size=shape, dtype=np.float32))
+    q, kt, vt = vals((w.B, n, w.Hq, w.d)), vals((w.B, n, w.Hkv, w.d)), vals((w.B, n, w.Hkv, w.d))
+    got = []
+    for page_seed in (None, 21):
+        dst = device_state(w, caps, poison=True, page_seed=page_seed)
+        anc = torch.zeros(w.B, n, dtype=torch.int64, device="cuda")
+        depth = torch.zeros(w.B, n, dtype=torch.int32, device="cuda")
+        err = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        tv.tv_build_tree_mask(torch.from_numpy(par).cuda(), anc, depth, err)
+        D = 7
+        out = torch.zeros(w.B, D, w.Hq, w.d, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(tv.tv_verify_attn_workspace_bytes(D, w.Hq, dst) // 4 + 64, dtype=torch.float32, device="cuda")
+        tv.tv_draft_attn(tv.to_device(q[:, :D], "bf16"), tv.to_device(kt[:, :D], "bf16"),
+                         tv.to_device(vt[:, :D], "bf16"), anc, err, dst, out, None, ws)
+        torch.cuda.synchronize()
+        got.append(out)
+    assert _equal(got[0], got[1])
+
+
+def test_missing_page_is_never_written_and_flags_the_sequence():
+    """A page-table entry out of range where a commit must write: refresh leaves that
+    sequence unchanged with TV_SEQ_BAD_PAGE; the other sequences refresh normally.
+    Compression of a prefix over such a page flags the sequence too."""
+    import torch
+    import tree_speculative_decoding_amd as tv
+    w = synth.Workload("pg5", 3, 8, 16, 2, 128, "bf16", (4, 128), 253, 1, 7, 1.0, 4005, prefix="raw")
+    _say("paged: missing page")
+    caps = pooled_caps(w, 64)
+    dst = device_state(w, caps, page_seed=9)
+    # sequence 1's C4 tile 1 (entries 64..127) holds the next commits (P = 253 -> n = 63):
+    # make its page id invalid
+    before_pt = dst.page_table[0].clone()
+    dst.page_table[0][1, 1] = dst.num_pages[0] + 7
+    before = [t.clone() for t in (dst.P, dst.n[0], dst.open_k[0], dst.tail_k)]
+    r = Runner(dst, w.D, w.Hq)
+    s = synth.step_inputs(w, 0)
+    r.step(upload_step(s, w.dtype))
+    torch.cuda.synchronize()
+    err = r.err.cpu().numpy()
+    assert err[1] == tv.TV_SEQ_BAD_PAGE and err[0] == 0 and err[2] == 0
+    assert dst.P[1] == before[0][1] and dst.n[0][1] == before[1][1]
+    assert torch.equal(dst.open_k[0][1], before[2][1]) and torch.equal(dst.tail_k[1], before[3][1])
+    assert (dst.P.cpu().numpy()[[0, 2]] > before[0].cpu().numpy()[[0, 2]]).all()
+    # compression over a missing page
+    st2 = tv.DeviceState(w.B, w.Hkv, w.d, w.dtype, w.levels, caps, page_seed=9)
+    st2.page_table[0].copy_(before_pt)
+    st2.page_table[0][2, 0] = -1
+    rk = np.stack([synth.raw_prefix(w, b)[0] for b in range(w.B)])
+    rv = np.stack([synth.raw_prefix(w, b)[1] for b in range(w.B)])
+    st2.P.fill_(w.P)
+    e2 = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    tv.tv_compress_prefix(st2, tv.to_device(rk, w.dtype), tv.to_device(rv, w.dtype), e2)
+    torch.cuda.synchronize()
+    assert e2.cpu().numpy().tolist() == [0, 0, tv.TV_SEQ_BAD_PAGE]

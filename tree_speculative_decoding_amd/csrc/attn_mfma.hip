@@ -59,8 +59,9 @@ __device__ __forceinline__ int v_slot(int e) {
 static __device__ __attribute__((aligned(256))) uint4 g_zero_chunk[1024];
 
 // At most 256 VGPRs: two workgroups per CU, each with two chunks (64 KB) in flight.  TT is
-// the number of 16-entry tiles the tail + tree chunk takes (its registers are sized by it).
-template <int NW, int TT>
+// the number of 16-entry tiles the tail + tree chunk takes (its registers are sized by it);
+// PAGED selects paged pools (a page-table read per chunk) over contiguous ones.
+template <int NW, int TT, bool PAGED>
 __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int PER = (1024 + NT - 1) / NT;   // K pieces (and V pieces) per thread
@@ -136,16 +137,19 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     // of a chunk are in bounds: every piece is loaded unconditionally (no data-dependent
     // code between the loads, so they are all in flight together) and entries past the
     // committed count are zeroed by selection when the chunk is written to LDS.
-    // Slots c >= c_hi (past the unit's stream) read the zero block.
-    auto load_chunk = [&](int c, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
+    // Slots c >= c_hi (past the unit's stream) read the zero block, and so does a chunk of a
+    // paged pool whose page id is out of range.  `pid` is the chunk's page (paged pools).
+    auto load_chunk = [&](int c, int pid, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
       const char* kb = (const char*)g_zero_chunk;
       const char* vb = kb;
       if (c < c_hi) {  // uniform
         int lvl, e0, cnt;
         chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
-        const uint32_t cap = (uint32_t)a.cap[lvl];
-        kb = (const char*)a.pk[lvl] + (bg * cap + e0) * (kDH * 2);   // K rows
-        vb = (const char*)a.pvt[lvl] + (bg * cap + e0) * (kDH * 2);  // V^T tile
+        if (!PAGED || (pid >= 0 && pid < (lvl == 0 ? a.npages[0] : a.npages[1]))) {
+          const size_t off = tile_offset(PAGED, pid, a.Hkv, a.cap[lvl], kDH, b, g, e0 >> 6) * 2;
+          kb = (const char*)a.pk[lvl] + off;   // K rows
+          vb = (const char*)a.pvt[lvl] + off;  // V^T tile
+        }
       }
 #pragma unroll
       for (int x = 0; x < PER; ++x) {
@@ -257,6 +261,22 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
       }
     };
 
+    // Page ids of paged pools: chunk c's page is read from the page table one step before
+    // its loads are issued, and ahead of that step's own chunk loads, so waiting for it
+    // never waits for chunk data.  Exactly one read per step (slots past the stream read
+    // the zero block), so the wait before a chunk counts the same loads on every path.
+    // Contiguous pools read nothing.
+    auto load_pid = [&](int c) -> int {
+      if (!PAGED) return 0;
+      const int32_t* src = (const int32_t*)g_zero_chunk;
+      if (c < c_hi) {  // uniform
+        const bool l1 = c >= T0;
+        src = (l1 ? a.pt[1] : a.pt[0]) + (size_t)b * (l1 ? a.ppseq[1] : a.ppseq[0]) + (l1 ? c - T0 : c);
+      }
+      return *src;
+    };
+    int pid_next = 0;  // page of the chunk the next step loads
+
     // One prefix chunk slot: if c is in the stream, write its chunk to LDS; refill the
     // slot's registers with chunk c + 2 (always issued, so that it is in flight with
     // chunk c + 1's loads); attend.
@@ -270,7 +290,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
         store_chunk(cnt, kpre, vpre);
         __syncthreads();
       }
-      load_chunk(c + 2, kpre, vpre);
+      const int pid = pid_next;
+      pid_next = load_pid(c + 3);
+      load_chunk(c + 2, pid, kpre, vpre);
       if (!have || !wave_has_rows) return;
       attend(cnt < 64, [&](int t, int i) { return 16 * t + 4 * grp + i >= cnt; });
     };
@@ -325,8 +347,12 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
       }
     }
 
-    load_chunk(c_lo, kpa, vpa);
-    load_chunk(c_lo + 1, kpb, vpb);
+    {
+      const int pid0 = load_pid(c_lo), pid1 = load_pid(c_lo + 1);
+      pid_next = load_pid(c_lo + 2);
+      load_chunk(c_lo, pid0, kpa, vpa);
+      load_chunk(c_lo + 1, pid1, kpb, vpb);
+    }
 
     if (tree_here) {
       __syncthreads();  // every wave is done with the LDS of the previous unit
@@ -465,9 +491,16 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   // past the G*D query rows skip the arithmetic.  One workgroup per slice.
   if (a.parts == 0) return hipSuccess;
   const int tt = a.fused_tree ? a.tree_tiles : 1;
-  if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1>), dim3(a.parts), dim3(256), 0, s, a);
-  else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2>), dim3(a.parts), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_attn_mfma<4, 4>), dim3(a.parts), dim3(256), 0, s, a);
+  const bool paged = a.pt[0] != nullptr;  // every level or none
+  if (paged) {
+    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, true>), dim3(a.parts), dim3(256), 0, s, a);
+    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, true>), dim3(a.parts), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_mfma<4, 4, true>), dim3(a.parts), dim3(256), 0, s, a);
+  } else {
+    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, false>), dim3(a.parts), dim3(256), 0, s, a);
+    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, false>), dim3(a.parts), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_mfma<4, 4, false>), dim3(a.parts), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

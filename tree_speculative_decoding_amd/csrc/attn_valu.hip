@@ -71,18 +71,23 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
       chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
       const T* pk = (const T*)a.pk[lvl];
       const T* pvt = (const T*)a.pvt[lvl];
-      const int cap = a.cap[lvl];
+      // the chunk is one 64-entry tile: contiguous by (b, g, tile), paged by its page id
+      const bool paged = a.pt[lvl] != nullptr;
+      const int tile = e0 >> 6;
+      const int page = paged ? a.pt[lvl][(size_t)b * a.ppseq[lvl] + tile] : 0;
+      const bool page_ok = !paged || (page >= 0 && page < a.npages[lvl]);
+      const size_t tb = tile_offset(paged, page, a.Hkv, a.cap[lvl], DH, b, g, tile);
       for (int sub = 0; sub * TK < cnt; ++sub) {
         const int base = e0 + sub * TK;
         const int n_sub = min(TK, cnt - sub * TK);
         __syncthreads();  // previous tile fully consumed (and Q staged on the first pass)
         for (int e = tid; e < TK * DH; e += 256) {
           const int k = e / DH, dd = e - k * DH;
-          Ks[k][dd] = k < n_sub ? Elem<T>::load(pk, (bg * cap + base + k) * DH + dd) : 0.f;
+          Ks[k][dd] = k < n_sub && page_ok ? Elem<T>::load(pk, tb + (size_t)((base + k) & 63) * DH + dd) : 0.f;
         }
         for (int e = tid; e < DH * TK; e += 256) {
           const int dd = e / TK, k = e - dd * TK;
-          Vs[dd][k] = k < n_sub ? Elem<T>::load(pvt, vt_index(bg * cap * DH, base + k, dd, DH)) : 0.f;
+          Vs[dd][k] = k < n_sub && page_ok ? Elem<T>::load(pvt, tb + (size_t)dd * 64 + ((base + k) & 63)) : 0.f;
         }
         __syncthreads();
         float sc[TK / 4];

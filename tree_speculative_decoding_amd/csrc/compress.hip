@@ -7,7 +7,8 @@
 // k_compress_entries: one thread per (entry, channel), channels fastest so the
 //   raw reads of a block are coalesced; sums in fp32 in position order.
 // k_compress_finish: one workgroup per (sequence, KV head): open-block sums, the
-//   finest level's raw tail, counts and the per-sequence status.
+//   finest level's raw tail, counts and the per-sequence status (a paged pool whose
+//   page table lacks a page the entries need flags the sequence TV_SEQ_BAD_PAGE).
 #include "tv_launch.h"
 
 namespace tv {
@@ -45,8 +46,11 @@ __global__ __launch_bounds__(256) void k_compress_entries(tv_state st, int l, co
     sk += Elem<T>::load(raw_k, o);
     sv += Elem<T>::load(raw_v, o);
   }
-  Elem<T>::store((T*)st.lvl[l].k, (((size_t)b * st.Hkv + g) * cap + j) * d + dd, sk / (float)C);
-  Elem<T>::store((T*)st.lvl[l].vt, vt_index(((size_t)b * st.Hkv + g) * cap * d, j, dd, d), sv / (float)C);
+  int page;
+  if (!tile_page(st.lvl[l], b, j >> 6, &page)) return;  // flagged by k_compress_finish
+  const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, st.Hkv, cap, d, b, g, j >> 6);
+  Elem<T>::store((T*)st.lvl[l].k, tb + (size_t)(j & 63) * d + dd, sk / (float)C);
+  Elem<T>::store((T*)st.lvl[l].vt, tb + (size_t)dd * 64 + (j & 63), sv / (float)C);
 }
 
 template <typename T>
@@ -57,7 +61,17 @@ __global__ __launch_bounds__(256) void k_compress_finish(tv_state st, const T* _
   const int d = st.d, Hkv = st.Hkv;
   const int P = st.P[b];
   int code;
-  const bool ok = prefix_ok(st, P, max_len, &code);
+  bool ok = prefix_ok(st, P, max_len, &code);
+  // every page the entries went to must exist (paged pools)
+  for (int l = 0; ok && l < st.n_levels; ++l)
+    for (int t = 0; t * 64 < P / st.lvl[l].C; ++t) {
+      int page;
+      if (!tile_page(st.lvl[l], b, t, &page)) {
+        ok = false;
+        code = TV_SEQ_BAD_PAGE;
+        break;
+      }
+    }
   if (g == 0 && threadIdx.x == 0) seq_err[b] = code;
   if (!ok) return;
   const size_t rbase = ((size_t)b * Hkv + g) * max_len;

@@ -5,7 +5,8 @@
 // their compression-intermediate buffers).
 //
 // One workgroup per sequence, one thread per (KV head, channel) up to 1024; the
-// accepted path is staged in LDS and checked once.  Every committed element is a bit
+// accepted path is staged in LDS and checked once, and so are the pages the commits
+// write (paged pools: a missing page leaves the sequence unchanged, TV_SEQ_BAD_PAGE).  Every committed element is a bit
 // copy: scratch
 // entries of the path nodes that close a block go to the next pool slots, the
 // path leaf's open-block sums replace the open sums, path tokens extend the raw
@@ -54,6 +55,17 @@ __global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch
     if (tid == 0) seq_err[b] = TV_SEQ_POOL_FULL;
     return;
   }
+  // every page the commits write must exist (paged pools), else nothing changes
+  bool page_bad = false;
+  for (int l = 0; l < L; ++l)
+    for (int j = P / st.lvl[l].C; j < P2 / st.lvl[l].C; ++j) {
+      int page;
+      page_bad |= !tile_page(st.lvl[l], b, j >> 6, &page);
+    }
+  if (page_bad) {
+    if (tid == 0) seq_err[b] = TV_SEQ_BAD_PAGE;
+    return;
+  }
   const int leaf = pth[m];
   for (int l = 0; l < L; ++l) {
     const int C = st.lvl[l].C, cap = st.lvl[l].cap;
@@ -64,11 +76,14 @@ __global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch
     const int j0 = P / C, j1 = P2 / C;
     for (int j = j0; j < j1; ++j) {
       const int u = pth[j * C + C - 1 - P];  // path node at the block's last position
+      int page;
+      tile_page(st.lvl[l], b, j >> 6, &page);  // checked above
       for (int e = tid; e < HD; e += nt) {
         const int g = e / d, dd = e - g * d;
         const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
-        pk[(((size_t)b * Hkv + g) * cap + j) * d + dd] = ek[src];
-        pvt[vt_index(((size_t)b * Hkv + g) * cap * d, j, dd, d)] = ev[src];
+        const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, Hkv, cap, d, b, g, j >> 6);
+        pk[tb + (size_t)(j & 63) * d + dd] = ek[src];
+        pvt[tb + (size_t)dd * 64 + (j & 63)] = ev[src];
       }
       if (commit_log != nullptr && tid == 0) {
         int32_t* row = commit_log + (((size_t)b * L + l) * D + (j - j0)) * 2;

@@ -52,10 +52,24 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// element offset of entry j, channel c of one (sequence, KV head) slice of a V pool
-// (64-entry tiles, transposed inside a tile)
-__device__ __forceinline__ size_t vt_index(size_t slice_base, int j, int c, int d) {
-  return slice_base + ((size_t)(j & ~63) * d) + (size_t)c * 64 + (j & 63);
+// Element offset of tile t (entries 64t .. 64t+63) of (sequence b, KV head g) in a
+// level's K or V^T pool (both hold 64*d elements per tile): contiguous pools by (b, g, t),
+// paged pools by the physical page `page` (the caller reads page_table[b][t]).
+__device__ __forceinline__ size_t tile_offset(bool paged, int page, int Hkv, int cap, int d, int b, int g,
+                                              int t) {
+  return paged ? ((size_t)page * Hkv + g) * 64 * d : (((size_t)b * Hkv + g) * cap + (size_t)t * 64) * d;
+}
+
+// Physical page of tile t of sequence b in a level (0 for a contiguous pool); false if the
+// page-table entry is outside [0, num_pages).
+__device__ __forceinline__ bool tile_page(const tv_level& L, int b, int t, int* page) {
+  if (L.page_table == nullptr) {
+    *page = 0;
+    return true;
+  }
+  const int p = L.page_table[(size_t)b * L.pages_per_seq + t];
+  *page = p;
+  return p >= 0 && p < L.num_pages;
 }
 
 // bits of the nodes 0..D-1 of a tree
@@ -80,6 +94,8 @@ struct AttnArgs {
   const void* pk[TV_MAX_LEVELS];     // pools, K row-major
   const void* pvt[TV_MAX_LEVELS];    // pools, V transposed
   const int32_t* pn[TV_MAX_LEVELS];
+  const int32_t* pt[TV_MAX_LEVELS];  // page tables (NULL: contiguous pool)
+  int ppseq[TV_MAX_LEVELS], npages[TV_MAX_LEVELS];
   const float* open_k[TV_MAX_LEVELS];
   const float* open_v[TV_MAX_LEVELS];
   const void* tail_k;

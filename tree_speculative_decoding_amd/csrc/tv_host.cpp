@@ -58,7 +58,15 @@ tv_status check_state(const tv_state* st) {
       return fail(TV_EINVAL, "level %d: NULL pool/count/open-sum pointer", l);
     if (!aligned16(L.k) || !aligned16(L.vt) || !aligned16(L.open_k) || !aligned16(L.open_v))
       return fail(TV_EINVAL, "level %d: pools and open sums must be 16-byte aligned", l);
+    if (L.page_table != nullptr) {
+      if (L.pages_per_seq < 0 || (long long)L.pages_per_seq * TV_POOL_ALIGN != L.cap)
+        return fail(TV_EINVAL, "level %d: paged pool needs cap = %d * pages_per_seq", l, TV_POOL_ALIGN);
+      if (L.num_pages < 1) return fail(TV_EINVAL, "level %d: num_pages = %d < 1", l, L.num_pages);
+    }
   }
+  for (int l = 1; l < st->n_levels; ++l)
+    if ((st->lvl[l].page_table == nullptr) != (st->lvl[0].page_table == nullptr))
+      return fail(TV_EINVAL, "either every level is paged or none is");
   if (st->n_levels > 0 && st->lvl[0].C > 1 && (!st->tail_k || !st->tail_v))
     return fail(TV_EINVAL, "tail pointers are NULL");
   if (!aligned16(st->tail_k) || !aligned16(st->tail_v)) return fail(TV_EINVAL, "tails must be 16-byte aligned");
@@ -161,6 +169,7 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
     a.C[l] = st->lvl[l].C; a.cap[l] = st->lvl[l].cap;
     a.pk[l] = st->lvl[l].k; a.pvt[l] = st->lvl[l].vt; a.pn[l] = st->lvl[l].n;
     a.open_k[l] = st->lvl[l].open_k; a.open_v[l] = st->lvl[l].open_v;
+    a.pt[l] = st->lvl[l].page_table; a.ppseq[l] = st->lvl[l].pages_per_seq; a.npages[l] = st->lvl[l].num_pages;
   }
   a.tail_k = st->tail_k; a.tail_v = st->tail_v; a.P = st->P;
   a.anc_ld = anc_ld;

@@ -21,7 +21,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tv.h")
 
 TV_OK, TV_EINVAL, TV_EUNSUPPORTED, TV_EWORKSPACE, TV_EHIP = 0, -1, -2, -3, -4
 TV_F32, TV_BF16 = 0, 1
-TV_SEQ_OK, TV_SEQ_BAD_PARENT, TV_SEQ_POOL_FULL, TV_SEQ_BAD_PREFIX, TV_SEQ_BAD_PATH = 0, 1, 2, 3, 4
+TV_SEQ_OK, TV_SEQ_BAD_PARENT, TV_SEQ_POOL_FULL, TV_SEQ_BAD_PREFIX, TV_SEQ_BAD_PATH, TV_SEQ_BAD_PAGE = 0, 1, 2, 3, 4, 5
 TV_MAX_LEVELS = 2
 TV_MAX_D = 64
 TV_POOL_ALIGN = 64
@@ -36,7 +36,8 @@ class TvError(RuntimeError):
 class TvLevel(ctypes.Structure):
     _fields_ = [("C", ctypes.c_int32), ("cap", ctypes.c_int32), ("k", ctypes.c_void_p),
                 ("vt", ctypes.c_void_p), ("n", ctypes.c_void_p), ("open_k", ctypes.c_void_p),
-                ("open_v", ctypes.c_void_p)]
+                ("open_v", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
+                ("pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32)]
 
 
 class TvState(ctypes.Structure):
@@ -162,10 +163,14 @@ def round_cap(n: int) -> int:
 
 class DeviceState:
     """Device tensors of a tv_state: pools (K row-major, V transposed), counts, open
-    sums, tail and committed lengths.  Allocation only; no arithmetic."""
+    sums, tail and committed lengths.  Allocation and data movement only; no arithmetic.
+
+    With ``page_seed`` set the pools are paged: each level holds B * cap/64 (+ ``spare_pages``)
+    physical pages of 64 entries for all KV heads, and a page table maps every
+    sequence's 64-entry tiles to a random permutation of them."""
 
     def __init__(self, B: int, Hkv: int, d: int, dtype: str, levels: Sequence[int],
-                 caps: Sequence[int], device="cuda"):
+                 caps: Sequence[int], device="cuda", page_seed: Optional[int] = None, spare_pages: int = 0):
         if len(levels) > TV_MAX_LEVELS:
             raise ValueError("at most two levels")
         self.B, self.Hkv, self.d, self.dtype = B, Hkv, d, dtype
@@ -173,8 +178,24 @@ class DeviceState:
         self.caps = tuple(round_cap(int(c)) for c in caps)
         td = torch_dtype(dtype)
         z = lambda *s, dt=td: torch.zeros(*s, dtype=dt, device=device)
-        self.pool_k = [z(B, Hkv, c, d) for c in self.caps]
-        self.pool_vt = [z(B, Hkv, c // TV_POOL_ALIGN, d, TV_POOL_ALIGN) for c in self.caps]
+        self.paged = page_seed is not None
+        A = TV_POOL_ALIGN
+        if self.paged:
+            rng = np.random.default_rng(page_seed)
+            self.page_table, self.num_pages = [], []
+            self.pool_k, self.pool_vt = [], []
+            for c in self.caps:
+                pps = c // A
+                npg = B * pps + spare_pages
+                perm = rng.permutation(npg)[: B * pps].reshape(B, pps).astype(np.int32)
+                self.page_table.append(torch.from_numpy(perm).to(device))
+                self.num_pages.append(npg)
+                self.pool_k.append(z(npg, Hkv, A, d))
+                self.pool_vt.append(z(npg, Hkv, d, A))
+        else:
+            self.page_table, self.num_pages = None, None
+            self.pool_k = [z(B, Hkv, c, d) for c in self.caps]
+            self.pool_vt = [z(B, Hkv, c // A, d, A) for c in self.caps]
         self.n = [z(B, dt=torch.int32) for _ in self.levels]
         self.open_k = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
         self.open_v = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
@@ -192,10 +213,46 @@ class DeviceState:
             L.k, L.vt = self.pool_k[l].data_ptr(), self.pool_vt[l].data_ptr()
             L.n = self.n[l].data_ptr()
             L.open_k, L.open_v = self.open_k[l].data_ptr(), self.open_v[l].data_ptr()
+            if self.paged:
+                L.page_table = self.page_table[l].data_ptr()
+                L.pages_per_seq = self.caps[l] // TV_POOL_ALIGN
+                L.num_pages = self.num_pages[l]
         s.tail_k = self.tail_k.data_ptr() if self.tail_k is not None else None
         s.tail_v = self.tail_v.data_ptr() if self.tail_v is not None else None
         s.P = self.P.data_ptr()
         return s
+
+
+    def write_seq(self, l: int, b: int, k: torch.Tensor, vt: torch.Tensor) -> None:
+        """Level l's entries of sequence b: k [Hkv][n][d] (n <= cap), vt the V tiles
+        [Hkv][cap/64][d][64] (tile_vt); both of the state's element type."""
+        A = TV_POOL_ALIGN
+        n = k.shape[1]
+        if not self.paged:
+            self.pool_k[l][b, :, :n] = k
+            self.pool_vt[l][b] = vt
+            return
+        pps = self.caps[l] // A
+        pages = self.page_table[l][b].long()
+        kk = torch.zeros(self.Hkv, self.caps[l], self.d, dtype=k.dtype, device=k.device)
+        kk[:, :n] = k
+        self.pool_k[l][pages] = kk.reshape(self.Hkv, pps, A, self.d).permute(1, 0, 2, 3)
+        self.pool_vt[l][pages] = vt.permute(1, 0, 2, 3)
+
+    def logical_k(self, l: int) -> torch.Tensor:
+        """Level l's K pool as [B][Hkv][cap][d] (a gather for a paged pool)."""
+        if not self.paged:
+            return self.pool_k[l]
+        A = TV_POOL_ALIGN
+        g = self.pool_k[l][self.page_table[l].long()]  # [B][pps][Hkv][64][d]
+        return g.permute(0, 2, 1, 3, 4).reshape(self.B, self.Hkv, self.caps[l], self.d)
+
+    def logical_vt(self, l: int) -> torch.Tensor:
+        """Level l's V tiles as [B][Hkv][cap/64][d][64] (a gather for a paged pool)."""
+        if not self.paged:
+            return self.pool_vt[l]
+        g = self.pool_vt[l][self.page_table[l].long()]  # [B][pps][Hkv][d][64]
+        return g.permute(0, 2, 1, 3, 4)
 
 
 class DeviceScratch:
