@@ -344,6 +344,7 @@ def main():
     }
     result["draft_tree"] = time_draft_tree(w, args.steps, stream)
     result["draft_attn"] = time_draft_attn(w, st, stream, reps=3)
+    result["paged_pool"] = time_paged(w, st, stream, reps=5)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -424,6 +425,54 @@ def time_draft_attn(w, st, stream, reps: int) -> dict:
         frac.append(round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
     return {"nodes_per_level": levels, "us_per_launch": us, "hbm_frac": frac, "expansion_nodes": n,
             "note": "same prefix stream as verify; rows for every node created so far"}
+
+
+def time_paged(w, st, stream, reps: int) -> dict:
+    """Gather cost of a paged pool: the benchmark's state copied into 64-entry pages at
+    random physical positions, then `reps` verify launches on each of the contiguous and
+    the paged state, alternating (same inputs, no refresh, so both stay equal)."""
+    import torch
+    import synth
+    import tree_speculative_decoding_amd as tv
+    A = 64
+    sp = tv.DeviceState(w.B, w.Hkv, w.d, w.dtype, w.levels, st.caps, page_seed=w.seed + 79)
+    for l in range(len(w.levels)):
+        pps = st.caps[l] // A
+        pages = sp.page_table[l].long().reshape(-1)
+        sp.pool_k[l][pages] = (st.pool_k[l].reshape(w.B, w.Hkv, pps, A, w.d).permute(0, 2, 1, 3, 4)
+                               .reshape(w.B * pps, w.Hkv, A, w.d))
+        sp.pool_vt[l][pages] = st.pool_vt[l].permute(0, 2, 1, 3, 4).reshape(w.B * pps, w.Hkv, w.d, A)
+        sp.n[l].copy_(st.n[l])
+        sp.open_k[l].copy_(st.open_k[l])
+        sp.open_v[l].copy_(st.open_v[l])
+    if st.tail_k is not None:
+        sp.tail_k.copy_(st.tail_k)
+        sp.tail_v.copy_(st.tail_v)
+    sp.P.copy_(st.P)
+    s = synth.step_inputs(w, 0)
+    i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+    q, kt, vt = tv.to_device(s.q, w.dtype), tv.to_device(s.k_tree, w.dtype), tv.to_device(s.v_tree, w.dtype)
+    anc = torch.zeros(w.B, w.D, dtype=torch.int64, device="cuda")
+    depth = torch.zeros(w.B, w.D, dtype=torch.int32, device="cuda")
+    err = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    tv.tv_build_tree_mask(i32(s.parents), anc, depth, err, stream)
+    out = [torch.empty(w.B, w.D, w.Hq, w.d, dtype=q.dtype, device="cuda") for _ in range(2)]
+    ws = torch.empty(tv.tv_verify_attn_workspace_bytes(w.D, w.Hq, st) // 4 + 64, dtype=torch.float32, device="cuda")
+    ms = {0: [], 1: []}
+    for i in range(reps + 1):
+        for which, state in ((0, st), (1, sp)):
+            a_, b_ = TimingEvent(), TimingEvent()
+            tv.tv_set_timing_events(a_, b_)
+            tv.tv_verify_attn(q, kt, vt, anc, depth, err, state, None, out[which], None, ws, 0, stream)
+            tv.tv_set_timing_events(None, None)
+            torch.cuda.synchronize()
+            if i > 0:  # the first round warms up
+                ms[which].append(a_.elapsed_ms(b_))
+    same = bool(torch.equal(out[0].view(torch.int16), out[1].view(torch.int16))) if w.dtype == "bf16" else \
+        bool(torch.equal(out[0], out[1]))
+    c, p_ = float(np.mean(ms[0])) * 1e3, float(np.mean(ms[1])) * 1e3
+    return {"contiguous_us": round(c, 1), "paged_us": round(p_, 1), "paged_over_contiguous": round(p_ / c, 4),
+            "page_entries": A, "outputs_bit_identical": same}
 
 
 def ctypes_ptr(x):
