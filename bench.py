@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="high_batch")
     ap.add_argument("--parts", type=int, default=0, help="prefix-stream workgroups (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the draft-tree, draft-attention and paged-pool measurements (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     ap.add_argument("--summarize-profiles", default="", metavar="DIR",
                     help="write profiles/*.md and the traffic JSON from rocprofv3 csv runs in DIR "
@@ -94,9 +96,9 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
 
 
-PROFILE_BENCH = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline"
-PROFILE_COUNTER_BENCH = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline"
-PREFIX_KERNEL = "tv::k_attn_mfma"
+PROFILE_BENCH = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras"
+PROFILE_COUNTER_BENCH = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras"
+PREFIX_KERNEL = "tv::k_attn_mfma<4, 1, false>"  # the contiguous-pool instance the benchmark runs
 
 
 def _counter_per_kernel(path: str, counter: str) -> dict:
@@ -342,9 +344,10 @@ def main():
         "seq_errors": errs,
         "setup_s": round(setup_s, 1),
     }
-    result["draft_tree"] = time_draft_tree(w, args.steps, stream)
-    result["draft_attn"] = time_draft_attn(w, st, stream, reps=3)
-    result["paged_pool"] = time_paged(w, st, stream, reps=5)
+    if not args.no_extras:
+        result["draft_tree"] = time_draft_tree(w, args.steps, stream)
+        result["draft_attn"] = time_draft_attn(w, st, stream, reps=3)
+        result["paged_pool"] = time_paged(w, st, stream, reps=5)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
