@@ -3,76 +3,125 @@
 // merge the prefix-stream partials of a query row, add the finest level's raw tail and
 // the node's own chain, and normalise.
 //
-// One workgroup of 16 waves per (sequence, KV head, 64-row block).  The D tree tokens
-// of that KV head are staged once in LDS.  Each wave owns 4 query rows (rows
-// r = node * G + head-in-group) and each lane d/64 channels of a row; the chain is the node's
-// ancestor mask and only its set bits are read, so K/V of other branches never enter
-// the arithmetic (excluded by selection, not by a -inf score).  Chain scores are
-// reduced eight at a time with interleaved shuffles, then folded into the same
-// base-2 online softmax as the prefix kernels.
+// One workgroup of 4 waves per (sequence, KV head, 16 rows of a 64-row block), one wave
+// per query row r = node * G + head-in-group, each lane d/64 channels of the row.  The
+// partials of a row are merged across lanes, not one after another: the lanes read the
+// slices' (max, sum) pairs together and reduce the common maximum M, then the partial
+// rows are read eight at a time with no load waiting on another and summed with weights
+// 2^(m_s - M) (slices with an empty sum weigh nothing, by selection).  For the paths
+// whose prefix kernel does not attend the tail and the chain, the D tree tokens of the
+// KV head are staged in LDS, and the chain is the node's ancestor mask: only its set
+// bits are read, so K/V of other branches never enter the arithmetic (excluded by
+// selection, not by a -inf score).  Chain scores are reduced eight at a time with
+// interleaved shuffles, then folded into the same base-2 online softmax as the prefix
+// kernels.
 #include "tv_launch.h"
 
 namespace tv {
 
+constexpr int kFinishWaves = 4;   // rows per workgroup
+constexpr int kMergeBatch = 16;   // partial rows read together
+
 template <typename T, int DH>
-__global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
+__global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
   constexpr int EPL = DH / 64;  // channels per lane
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   T* kt_s = (T*)lds_raw;                         // [D][DH]
   T* vt_s = kt_s + (size_t)a.D * DH;             // [D][DH]
 
+  constexpr int kGroups = 64 / kFinishWaves;     // workgroups per 64-row block
   const int g = blockIdx.x % a.Hkv;
-  const int rb = blockIdx.x / a.Hkv;
+  const int rb = blockIdx.x / a.Hkv / kGroups;
+  const int rg = blockIdx.x / a.Hkv % kGroups;
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t bg = (size_t)b * a.Hkv + g;
   const bool bad = a.seq_err != nullptr && a.seq_err[b] != TV_SEQ_OK;
   T* out = (T*)a.out;
 
-  // stage the tree tokens of this KV head
-  const T* ktg = (const T*)a.k_tree;
-  const T* vtg = (const T*)a.v_tree;
-  for (int e = tid; e < a.D * DH; e += blockDim.x) {
-    const int j = e / DH, c = e - j * DH;
-    const size_t o = (((size_t)b * a.D + j) * a.Hkv + g) * DH + c;
-    kt_s[e] = ktg[o];
-    vt_s[e] = vtg[o];
+  if (!a.fused_tree) {  // stage the tree tokens of this KV head
+    const T* ktg = (const T*)a.k_tree;
+    const T* vtg = (const T*)a.v_tree;
+    for (int e = tid; e < a.D * DH; e += blockDim.x) {
+      const int j = e / DH, c = e - j * DH;
+      const size_t o = (((size_t)b * a.D + j) * a.Hkv + g) * DH + c;
+      kt_s[e] = ktg[o];
+      vt_s[e] = vtg[o];
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   const uint64_t nodes = node_mask(a.D);
   const T* q = (const T*)a.q;
-  for (int k = 0; k < 4; ++k) {
-    const int r = rb * 64 + w * 4 + k;
-    if (r >= a.R) break;  // wave-uniform
+  {
+    const int r = rb * 64 + rg * kFinishWaves + w;
+    if (r >= a.R) return;  // wave-uniform; no barrier follows
     const int i = r / a.G, hh = r - i * a.G, h = g * a.G + hh;
     const size_t obase = (((size_t)b * a.D + i) * a.Hq + h) * DH + lane * EPL;
     if (bad) {
 #pragma unroll
       for (int x = 0; x < EPL; ++x) Elem<T>::store(out, obase + x, 0.f);
       if (a.lse != nullptr && lane == 0) a.lse[((size_t)b * a.D + i) * a.Hq + h] = -INFINITY;
-      continue;
+      return;
     }
     // partials of the shared prefix: one per workgroup whose slice touched this unit
     const long long u = (long long)bg * a.row_blocks + rb;
     const int n_parts = a.parts > 0 ? unit_part_count(u, a.tmax, a.per) : 0;
     // with the tail and chain attended by the prefix kernel, a unit it covered with one
     // workgroup is already written; otherwise its partials already hold tail and chain
-    if (a.fused_tree && n_parts == 1) continue;
+    if (a.fused_tree && n_parts == 1) return;
     float m = -INFINITY, l = 0.f, o[EPL];
 #pragma unroll
     for (int x = 0; x < EPL; ++x) o[x] = 0.f;
-    for (int s = 0; s < n_parts; ++s) {
-      const size_t wrow = (bg * a.smax + s) * a.R + r;
-      const float2 ml = a.ws_ml[wrow];
-      if (ml.y > 0.f) {
-        const float mn = fmaxf(m, ml.x);
-        const float ca = exp2f(m - mn), cb = exp2f(ml.x - mn);
-        l = l * ca + ml.y * cb;
+    const size_t row0 = bg * a.smax * a.R + r;  // slice s of this row: row0 + s * R
+    // (max, sum) of slice s0 + lane; lanes past the last slice read the last one's and
+    // drop it by selection
+    auto slice_ml = [&](int s0) {
+      const int s = min(s0 + lane, n_parts - 1);
+      float2 ml = a.ws_ml[row0 + (size_t)s * a.R];
+      asm volatile("" ::"v"(ml.x), "v"(ml.y));
+      if (s0 + lane >= n_parts) ml.y = 0.f;
+      return ml;
+    };
+    float2 ml0 = make_float2(-INFINITY, 0.f);
+    float M = -INFINITY;
+    for (int s0 = 0; s0 < n_parts; s0 += 64) {
+      const float2 ml = slice_ml(s0);
+      if (s0 == 0) ml0 = ml;
+      if (ml.y > 0.f) M = fmaxf(M, ml.x);
+    }
+    M = wave_max(M);
+    if (M != -INFINITY) {  // wave-uniform: some slice saw a visible entry
+      float L = 0.f;
+      for (int s0 = 0; s0 < n_parts; s0 += 64) {
+        const float2 ml = s0 == 0 ? ml0 : slice_ml(s0);
+        const float c = ml.y > 0.f ? exp2f(ml.x - M) : 0.f;
+        L = fmaf(c, ml.y, L);
+        const int cnt = min(64, n_parts - s0);
+        for (int t0 = 0; t0 < cnt; t0 += kMergeBatch) {
+          float v[kMergeBatch][EPL], ct[kMergeBatch];
 #pragma unroll
-        for (int x = 0; x < EPL; ++x) o[x] = o[x] * ca + a.ws_o[wrow * DH + lane * EPL + x] * cb;
-        m = mn;
+          for (int t = 0; t < kMergeBatch; ++t) {
+            const int tt = min(t0 + t, cnt - 1);  // in range; weight 0 past cnt
+            ct[t] = t0 + t < cnt ? __shfl(c, tt, 64) : 0.f;
+            const float* src = a.ws_o + (row0 + (size_t)(s0 + tt) * a.R) * DH + lane * EPL;
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) v[t][x] = src[x];
+          }
+          // every load above is issued before any is used (none may move under the
+          // selections below)
+#pragma unroll
+          for (int t = 0; t < kMergeBatch; ++t)
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) asm volatile("" ::"v"(v[t][x]));
+#pragma unroll
+          for (int t = 0; t < kMergeBatch; ++t)
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) o[x] = ct[t] > 0.f ? fmaf(ct[t], v[t][x], o[x]) : o[x];
+        }
       }
+      m = M;
+      l = wave_sum(L);
     }
 
     float qv[EPL];
@@ -156,18 +205,17 @@ __global__ __launch_bounds__(1024) void k_attn_finish(AttnArgs a) {
     for (int x = 0; x < EPL; ++x) Elem<T>::store(out, obase + x, o[x] * inv);
     if (a.lse != nullptr && lane == 0) a.lse[((size_t)b * a.D + i) * a.Hq + h] = (m + log2f(l)) * kLn2;
   }
-
 }
 
 template <typename T, int DH>
 static hipError_t launch_finish_t(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)a.D * DH * sizeof(T) * 2;
+  const size_t lds = a.fused_tree ? 0 : (size_t)a.D * DH * sizeof(T) * 2;
   if (lds > 65536) {  // beyond the default dynamic-LDS limit (fp32, d = 128, D > 32)
     hipError_t e = hipFuncSetAttribute((const void*)k_attn_finish<T, DH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(a.Hkv * a.row_blocks, a.B), block(1024);
+  dim3 grid(a.Hkv * a.row_blocks * (64 / kFinishWaves), a.B), block(kFinishWaves * 64);
   hipLaunchKernelGGL((k_attn_finish<T, DH>), grid, block, lds, s, a);
   return hipGetLastError();
 }

@@ -203,8 +203,16 @@ class DeviceState:
         self.tail_k = z(B, Hkv, c0 - 1, d) if c0 > 1 else None
         self.tail_v = z(B, Hkv, c0 - 1, d) if c0 > 1 else None
         self.P = z(B, dt=torch.int32)
+        self._struct = None
 
     def struct(self) -> TvState:
+        """The tv_state of these tensors.  They are allocated once and only ever updated
+        in place, so the pointers are taken once (a copy is returned: callers may edit it)."""
+        if self._struct is None:
+            self._struct = self._make_struct()
+        return TvState.from_buffer_copy(self._struct)
+
+    def _make_struct(self) -> TvState:
         s = TvState()
         s.B, s.Hkv, s.d, s.dtype, s.n_levels = self.B, self.Hkv, self.d, tv_dtype(self.dtype), len(self.levels)
         for l, C in enumerate(self.levels):
@@ -264,8 +272,15 @@ class DeviceScratch:
         self.entry_v = [torch.zeros(B, D, Hkv, d, dtype=td, device=device) for _ in range(n_levels)]
         self.open_k = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
         self.open_v = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
+        self._struct = None
 
     def struct(self) -> TvScratch:
+        """The tv_scratch of these tensors (pointers taken once, as for DeviceState)."""
+        if self._struct is None:
+            self._struct = self._make_struct()
+        return TvScratch.from_buffer_copy(self._struct)
+
+    def _make_struct(self) -> TvScratch:
         s = TvScratch()
         for l in range(len(self.entry_k)):
             s.entry_k[l] = self.entry_k[l].data_ptr()
@@ -276,7 +291,19 @@ class DeviceScratch:
 
 
 def _state(st) -> TvState:
-    return st.struct() if isinstance(st, DeviceState) else st
+    if isinstance(st, DeviceState):
+        if st._struct is None:
+            st._struct = st._make_struct()
+        return st._struct
+    return st
+
+
+def _scratch(sc) -> Optional[TvScratch]:
+    if isinstance(sc, DeviceScratch):
+        if sc._struct is None:
+            sc._struct = sc._make_struct()
+        return sc._struct
+    return sc
 
 
 # ----------------------------------------------------------------------------- entry points
@@ -308,7 +335,7 @@ def tv_verify_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, 
                    num_parts: int = 0, stream=None) -> None:
     B, D, Hq, d = q.shape
     s = _state(st)
-    sc = scratch.struct() if isinstance(scratch, DeviceScratch) else scratch
+    sc = _scratch(scratch)
     _check(lib().tv_verify_attn(D, Hq, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(anc), _ptr(depth),
                                 _ptr(seq_err), ctypes.byref(s),
                                 ctypes.byref(sc) if sc is not None else None, _ptr(out), _ptr(lse),
@@ -338,7 +365,7 @@ def tv_accept(parents, anc, depth, draft_tok, target_tok, seq_err, m, path, bonu
 def tv_refresh_state(st, scratch, k_tree, v_tree, m, path, commit_log, seq_err, stream=None) -> None:
     D = k_tree.shape[1]
     s = _state(st)
-    sc = scratch.struct() if isinstance(scratch, DeviceScratch) else scratch
+    sc = _scratch(scratch)
     _check(lib().tv_refresh_state(D, ctypes.byref(s), ctypes.byref(sc) if sc is not None else None,
                                   _ptr(k_tree), _ptr(v_tree), _ptr(m), _ptr(path), _ptr(commit_log),
                                   _ptr(seq_err), _stream(stream)))
