@@ -15,6 +15,12 @@ decoding.  Prints one JSON line:
                  events on its stream, vs 8 TB/s
   cpu_baseline   the fp64 oracle timed on this host for a bounded sample of the
                  same workload (rank 0, N = 1 only)
+  read_ceiling   a plain HIP read-reduce over 4 GiB on the same device (the practical
+                 HBM read ceiling) and the attention kernel's fraction of it
+
+    python bench.py --sweep OUT.md [--steps K] [--warmup W]
+
+runs the long-context budget sweep instead (see sweep()).
 """
 from __future__ import annotations
 
@@ -39,7 +45,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps first (kernel times drift for the first ~10 ms of a busy period)")
     ap.add_argument("--workload", default="high_batch")
     ap.add_argument("--parts", type=int, default=0, help="prefix-stream workgroups (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -49,6 +56,10 @@ def parse():
     ap.add_argument("--summarize-profiles", default="", metavar="DIR",
                     help="write profiles/*.md and the traffic JSON from rocprofv3 csv runs in DIR "
                          "(kt/, FETCH_SIZE/, WRITE_SIZE/, copy_FETCH_SIZE/, copy_WRITE_SIZE/, kt.txt)")
+    ap.add_argument("--sweep", default="", metavar="OUT_MD",
+                    help="run the long-context budget sweep instead (D 5..8 x batch 1..64 x top-k 1, 2 at a "
+                         "131072-token prefix) and write its table to OUT_MD; one JSON line per point")
+    ap.add_argument("--sweep-batches", default="1,4,16,64", help="batch sizes of the sweep (comma-separated)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (to scale HBM byte counters)")
     return ap.parse_args()
@@ -210,6 +221,138 @@ def measured_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def pooled_state(w, caps, draw_seqs=None):
+    """Device state of workload w at step 0 with the committed compressed entries drawn
+    directly (synth.pooled_prefix); device sequence i holds the workload's sequence
+    draw_seqs[i] (default: i)."""
+    import concurrent.futures as cf
+    import synth
+    import tree_speculative_decoding_amd as tv
+    seqs = list(range(w.B)) if draw_seqs is None else list(draw_seqs)
+    st = tv.DeviceState(len(seqs), w.Hkv, w.d, w.dtype, w.levels, caps)
+
+    def draw(b):
+        return [(k, tv.tv.tile_vt(v, st.caps[l])) for l, (k, v) in enumerate(synth.pooled_prefix(w, b))]
+
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        for i, lv in enumerate(ex.map(draw, seqs)):
+            for l, (k, vt) in enumerate(lv):
+                st.write_seq(l, i, tv.to_device(k, w.dtype), tv.to_device(vt, w.dtype))
+                st.n[l][i] = k.shape[1]
+    st.P.fill_(w.P)
+    return st
+
+
+class StepRunner:
+    """Per-step buffers of one (B, D, Hq) shape and the four calls of one step on `stream`."""
+
+    def __init__(self, w, st, parts: int, stream):
+        import torch
+        import tree_speculative_decoding_amd as tv
+        B, D, Hq, Hkv, d, dev = st.B, w.D, w.Hq, w.Hkv, w.d, "cuda"
+        self.w, self.parts, self.stream = w, parts, stream
+        self.anc = torch.zeros(B, D, dtype=torch.int64, device=dev)
+        self.depth = torch.zeros(B, D, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.out = torch.zeros(B, D, Hq, d, dtype=tv.tv.torch_dtype(w.dtype), device=dev)
+        self.lse = torch.zeros(B, D, Hq, dtype=torch.float32, device=dev)
+        self.m = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.path = torch.zeros(B, D, dtype=torch.int32, device=dev)
+        self.bonus = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.log = torch.zeros(B, len(w.levels), D, 2, dtype=torch.int32, device=dev)
+        self.sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels))
+        self.ws = torch.empty(tv.tv_verify_attn_workspace_bytes(D, Hq, st, parts) // 4 + 64, dtype=torch.float32,
+                              device=dev)
+
+    def inputs(self, t: int, batch=None) -> dict:
+        import torch
+        import synth
+        import tree_speculative_decoding_amd as tv
+        s = synth.step_inputs(self.w, t, batch=batch)
+        i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+        return dict(parents=i32(s.parents), draft=i32(s.draft), target=i32(s.target),
+                    q=tv.to_device(s.q, self.w.dtype), kt=tv.to_device(s.k_tree, self.w.dtype),
+                    vt=tv.to_device(s.v_tree, self.w.dtype))
+
+    def step(self, st, x: dict):
+        import tree_speculative_decoding_amd as tv
+        s = self.stream
+        tv.tv_build_tree_mask(x["parents"], self.anc, self.depth, self.err, s)
+        tv.tv_verify_attn(x["q"], x["kt"], x["vt"], self.anc, self.depth, self.err, st, self.sc, self.out, self.lse,
+                          self.ws, self.parts, s)
+        tv.tv_accept(x["parents"], self.anc, self.depth, x["draft"], x["target"], self.err, self.m, self.path,
+                     self.bonus, s)
+        tv.tv_refresh_state(st, self.sc, x["kt"], x["vt"], self.m, self.path, self.log, self.err, s)
+
+
+def record(ev: "TimingEvent", stream) -> None:
+    if TimingEvent._hip.hipEventRecord(ctypes_ptr(ev.handle), ctypes_ptr(stream.cuda_stream)) != 0:
+        raise RuntimeError("hipEventRecord failed")
+
+
+def settle_warmup(runner: StepRunner, states: list, sets: list, warmup: int, settle_ms: float = 15.0) -> int:
+    """Untimed steps to run before timing: at least `warmup`, and enough to keep the GPU
+    busy for `settle_ms` (measured launches run up to ~15% slower a few ms into a busy
+    period, then settle), from a 3-step estimate of the step time."""
+    import torch
+    a_, b_ = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    record(a_, runner.stream)
+    for t in range(3):
+        runner.step(states[t % len(states)], sets[t % len(sets)])
+    record(b_, runner.stream)
+    torch.cuda.synchronize()
+    per = max(a_.elapsed_ms(b_) / 3.0, 1e-3)
+    return max(warmup, min(SWEEP_MAX_WARMUP, int(math.ceil(settle_ms / per))))
+
+
+def timed_steps(runner: StepRunner, states: list, sets: list, warmup: int, steps: int) -> dict:
+    """`warmup` untimed steps, then `steps` timed ones, rotating over `states` (so that a
+    small working set is read cold from HBM each step) and the input `sets`.  Returns the
+    whole region's time, per-step times (fence-free events between steps), the attention
+    kernel's per-launch times (events the library records around it) and the committed
+    lengths before and after the timed steps."""
+    import torch
+    import tree_speculative_decoding_amd as tv
+    stream = runner.stream
+    attn_ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    step_ev = [TimingEvent() for _ in range(steps + 1)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for t in range(warmup):
+        runner.step(states[t % len(states)], sets[t % len(sets)])
+    torch.cuda.synchronize()
+    n_before = [sum(int(x.sum()) for x in st.n) for st in states]
+    P_before = [st.P.clone() for st in states]
+    torch.cuda.synchronize()
+    start.record(stream)
+    for t in range(steps):
+        record(step_ev[t], stream)
+        tv.tv_set_timing_events(attn_ev[t][0], attn_ev[t][1])
+        runner.step(states[(warmup + t) % len(states)], sets[(warmup + t) % len(sets)])
+    record(step_ev[steps], stream)
+    stop.record(stream)
+    tv.tv_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    return {"total_ms": start.elapsed_time(stop),
+            "step_ms": [step_ev[t].elapsed_ms(step_ev[t + 1]) for t in range(steps)],
+            "attn_ms": [a_.elapsed_ms(b_) for a_, b_ in attn_ev],
+            "n_before": n_before, "n_after": [sum(int(x.sum()) for x in st.n) for st in states],
+            "P_advance": sum(int((st.P - p0).sum()) for st, p0 in zip(states, P_before))}
+
+
+def attn_bytes_per_launch(w, B: int, entries_per_seq_head: float, tail: float) -> float:
+    """Algorithmic bytes of one verify-attention launch: every committed entry's K and V
+    once, the raw tail (< C0 tokens), Q in, O out, the tree tokens' K and V, and the plan
+    (parents, mask, depth: 16 B per node)."""
+    e = 2 if w.dtype == "bf16" else 4
+    return B * (w.Hkv * (entries_per_seq_head + tail) * w.d * 2 * e + w.D * w.Hq * w.d * 2 * e
+                + w.D * w.Hkv * w.d * 2 * e + 16 * w.D)
+
+
+def pct(xs, q) -> float:
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -223,6 +366,9 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
         return
+    if args.sweep:
+        sweep(args)
+        return
 
     import torch
 
@@ -230,94 +376,33 @@ def main():
     import tree_speculative_decoding_amd as tv
 
     w = synth.WORKLOADS[args.workload]
-    dev = "cuda"
     torch.cuda.set_device(0)
-    B, D, Hq, Hkv, d = w.B, w.D, w.Hq, w.Hkv, w.d
-    e = 2 if w.dtype == "bf16" else 4
+    B, D = w.B, w.D
     total_steps = args.warmup + args.steps
     caps = [tv.round_cap(w.P // C + math.ceil(total_steps * D / C) + 2) for C in w.levels]
 
-    # ---- persistent state: committed compressed entries drawn directly (pooled prefix)
+    # persistent state (committed compressed entries drawn directly) and N_INPUT_SETS
+    # per-step input sets, rotated; all resident before timing
     t0 = time.time()
-    st = tv.DeviceState(B, Hkv, d, w.dtype, w.levels, caps)
-    import concurrent.futures as cf
-
-    def draw(b):
-        return [(k, tv.tv.tile_vt(v, st.caps[l])) for l, (k, v) in enumerate(synth.pooled_prefix(w, b))]
-
-    with cf.ThreadPoolExecutor(max_workers=8) as ex:
-        for b, lv in enumerate(ex.map(draw, range(B))):
-            for l, (k, vt) in enumerate(lv):
-                st.write_seq(l, b, tv.to_device(k, w.dtype), tv.to_device(vt, w.dtype))
-                st.n[l][b] = k.shape[1]
-    st.P.fill_(w.P)
-
-    # ---- per-step inputs (N_INPUT_SETS sets, rotated)
-    sets = []
-    for t in range(N_INPUT_SETS):
-        s = synth.step_inputs(w, t)
-        i32 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
-        sets.append(dict(parents=i32(s.parents), draft=i32(s.draft), target=i32(s.target),
-                         q=tv.to_device(s.q, w.dtype), kt=tv.to_device(s.k_tree, w.dtype),
-                         vt=tv.to_device(s.v_tree, w.dtype)))
-    anc = torch.zeros(B, D, dtype=torch.int64, device=dev)
-    depth = torch.zeros(B, D, dtype=torch.int32, device=dev)
-    err = torch.zeros(B, dtype=torch.int32, device=dev)
-    out = torch.zeros(B, D, Hq, d, dtype=tv.tv.torch_dtype(w.dtype), device=dev)
-    lse = torch.zeros(B, D, Hq, dtype=torch.float32, device=dev)
-    m = torch.zeros(B, dtype=torch.int32, device=dev)
-    path = torch.zeros(B, D, dtype=torch.int32, device=dev)
-    bonus = torch.zeros(B, dtype=torch.int32, device=dev)
-    log = torch.zeros(B, len(w.levels), D, 2, dtype=torch.int32, device=dev)
-    sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels))
-    ws_bytes = tv.tv_verify_attn_workspace_bytes(D, Hq, st, args.parts)
-    ws = torch.empty(ws_bytes // 4 + 64, dtype=torch.float32, device=dev)
+    st = pooled_state(w, caps)
     stream = torch.cuda.current_stream()
+    runner = StepRunner(w, st, args.parts, stream)
+    sets = [runner.inputs(t) for t in range(N_INPUT_SETS)]
+    saved = snapshot(st)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    def one_step(x):
-        tv.tv_build_tree_mask(x["parents"], anc, depth, err, stream)
-        tv.tv_verify_attn(x["q"], x["kt"], x["vt"], anc, depth, err, st, sc, out, lse, ws, args.parts, stream)
-        tv.tv_accept(x["parents"], anc, depth, x["draft"], x["target"], err, m, path, bonus, stream)
-        tv.tv_refresh_state(st, sc, x["kt"], x["vt"], m, path, log, err, stream)
+    r = timed_steps(runner, [st], sets, args.warmup, args.steps)
+    ms_step = r["total_ms"] / args.steps
+    attn_avg_ms = float(np.mean(r["attn_ms"]))
+    accepted = r["P_advance"] / B / args.steps  # mean m + 1 per step
 
-    for t in range(args.warmup):
-        one_step(sets[t % N_INPUT_SETS])
-    torch.cuda.synchronize()
-
-    # per-launch events around the prefix kernel (recorded by the library on `stream`)
-    ev = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
-    n_sum_before = sum(int(x.sum()) for x in st.n)
-    P_before = st.P.clone()
-    acc_len = torch.zeros(B, dtype=torch.int64, device=dev)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for t in range(args.steps):
-        tv.tv_set_timing_events(ev[t][0], ev[t][1])
-        one_step(sets[(args.warmup + t) % N_INPUT_SETS])
-    stop.record(stream)
-    tv.tv_set_timing_events(None, None)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-    attn_ms = [a_.elapsed_ms(b_) for a_, b_ in ev]
-    attn_avg_ms = float(np.mean(attn_ms))
-    n_sum_after = sum(int(x.sum()) for x in st.n)
-    accepted = (st.P - P_before).double().mean().item() / args.steps  # mean m + 1 per step
-
-    # Algorithmic bytes of the attention kernel per launch: every committed entry's K and
-    # V once (averaged over the timed steps as the pools grow), the raw tail (< C0
-    # tokens), Q in, O out, the tree tokens' K and V, and the plan (parents, mask, depth:
-    # 16 B per node).  The prefix kernel reads all of these and writes every output row
-    # itself when each (sequence, head) prefix is one workgroup's whole slice.
-    entries_per_seq_head = (n_sum_before + n_sum_after) / 2.0 / B
-    tail = float((P_before % w.levels[0]).float().mean().item()) if w.levels[0] > 1 else 0.0
-    attn_bytes = B * (Hkv * (entries_per_seq_head + tail) * d * 2 * e + D * Hq * d * 2 * e
-                      + D * Hkv * d * 2 * e + 16 * D)
+    # the pools grow during the timed steps: their entries are averaged over the steps
+    entries_per_seq_head = (r["n_before"][0] + r["n_after"][0]) / 2.0 / B
+    tail = float((st.P % w.levels[0]).float().mean().item()) if w.levels[0] > 1 else 0.0
+    attn_bytes = attn_bytes_per_launch(w, B, entries_per_seq_head, tail)
     achieved = attn_bytes / (attn_avg_ms * 1e-3) / 1e9
-    errs = int((err != 0).sum())
+    errs = int((runner.err != 0).sum())
 
     result = {
         "metric": "verified tree tokens/sec at D=8 bs=64 + achieved HBM GB/s fraction of peak",
@@ -332,7 +417,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "D": D, "Hq": Hq, "Hkv": Hkv, "head_dim": d,
+        "config": {"workload": w.name, "B": B, "D": D, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d,
                    "prefix_tokens": w.P, "levels": list(w.levels), "tree": w.spec_name,
                    "p_agree": w.p_agree, "prefix_workgroups": args.parts or "auto",
                    "parallelism": "single GPU"},
@@ -340,17 +425,215 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
                      "kernel": "k_attn_mfma (prefix stream + tail + chain)", "avg_launch_ms": round(attn_avg_ms, 5),
                      "algorithmic_bytes_per_launch": int(attn_bytes)},
+        "step_ms_p10_p50_p90": [round(pct(r["step_ms"], q), 4) for q in (10, 50, 90)],
+        "attn_ms_p10_p50_p90": [round(pct(r["attn_ms"], q), 4) for q in (10, 50, 90)],
         "accepted_length": round(accepted, 4),
         "seq_errors": errs,
         "setup_s": round(setup_s, 1),
     }
     if not args.no_extras:
+        # the same timed steps from the same starting state, captured in one HIP graph
+        graph_ms = graph_step_ms(runner, [st], sets, args.steps, [st], [saved])
+        result["graph_ms_per_step"] = round(graph_ms, 4)
+        result["graph_tokens_per_s"] = round(B * D / (graph_ms * 1e-3), 1)
+        ceiling = read_ceiling(stream)
+        ceiling["attn_frac_of_ceiling"] = round(achieved / ceiling["GB/s"], 4)
+        result["read_ceiling"] = ceiling
         result["draft_tree"] = time_draft_tree(w, args.steps, stream)
         result["draft_attn"] = time_draft_attn(w, st, stream, reps=3)
         result["paged_pool"] = time_paged(w, st, stream, reps=5)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def read_ceiling(stream, gib: int = 4) -> dict:
+    """The device's practical HBM read ceiling: a plain read-reduce kernel (libtv_measure.so)
+    over `gib` GiB, launched with 2, 4 and 8 workgroups per CU, 5 timed launches each
+    (fence-free events on `stream`); the best average."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "tree_speculative_decoding_amd", "libtv_measure.so"))
+    lib.tvm_read_stream.restype = ctypes.c_int
+    lib.tvm_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(cus * 8, dtype=torch.int32, device="cuda")
+    best, rows = 0.0, {}
+    for per_cu in (2, 4, 8):
+        launch = lambda: lib.tvm_read_stream(buf.data_ptr(), nbytes, cus * per_cu, sink.data_ptr(),
+                                             stream.cuda_stream)
+        if launch() != 0:
+            raise RuntimeError("tvm_read_stream failed")
+        ev = [(TimingEvent(), TimingEvent()) for _ in range(5)]
+        for a_, b_ in ev:
+            record(a_, stream)
+            launch()
+            record(b_, stream)
+        torch.cuda.synchronize()
+        gbs = nbytes / (float(np.mean([a_.elapsed_ms(b_) for a_, b_ in ev])) * 1e-3) / 1e9
+        rows[f"{per_cu}_per_cu"] = round(gbs, 1)
+        best = max(best, gbs)
+    del buf
+    torch.cuda.empty_cache()
+    return {"GB/s": round(best, 1), "frac_of_peak": round(best / PEAK_HBM_GBS, 4), "bytes": nbytes,
+            "by_workgroups": rows, "kernel": "plain read-reduce, 16-byte loads, 8 in flight per thread"}
+
+
+SWEEP_P = 131072
+SWEEP_MAX_WARMUP = 400  # steps; 15 ms at the fastest point (B=1, ~40 us of attention) needs < 400
+
+
+def sweep(args) -> None:
+    """Long-context budget sweep: D in 5..8 x batch in {1, 4, 16, 64} x top-k {1, 2} (k=1:
+    a chain of D-1 draft steps; k=2: 3 steps pruned to D), 64/8 heads, d=128, bf16,
+    131072-token prefix (32768 C4 + 1024 C128 entries).  Agreement p only changes the
+    accepted length, so each (D, B, k) is timed once per p in {0.5, 0.7} with that
+    point's own trees and tokens.  The committed state is drawn once per batch size and
+    restored before every point; when one state is under 1 GiB, ceil(1 GiB / size) + 1
+    states (different sequences) are rotated so every step reads cold from HBM, and the
+    same point is also timed warm (one state, back to back), labelled so.  Writes a
+    markdown table to args.sweep and prints one JSON line per point."""
+    import torch
+    import synth
+    import tree_speculative_decoding_amd as tv
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    keep = {int(x) for x in args.sweep_batches.split(",") if x}
+    points = [w for w in synth.sweep_workloads() if w.B in keep]
+    steps, warmup = args.steps, args.warmup
+    ceiling = read_ceiling(stream)
+    rows = []
+    for B in sorted({w.B for w in points}):
+        ws_ = [w for w in points if w.B == B]
+        w0 = ws_[0]
+        extra = (steps + max(warmup, SWEEP_MAX_WARMUP)) * max(w.D for w in ws_)
+        caps = [tv.round_cap(SWEEP_P // C + math.ceil(extra / C) + 2) for C in w0.levels]
+        per_state = B * w0.Hkv * sum(caps) * w0.d * 2 * 2
+        n_rot = math.ceil((1 << 30) / per_state) + 1 if per_state < (1 << 30) else 1
+        t0 = time.time()
+        states = [pooled_state(w0.with_(B=B * n_rot), caps, range(r * B, (r + 1) * B)) for r in range(n_rot)]
+        saved = [snapshot(st) for st in states]
+        torch.cuda.synchronize()
+        print(f"# batch {B}: {n_rot} state(s) of {per_state / 1e9:.3f} GB, {time.time() - t0:.1f} s", file=sys.stderr,
+              flush=True)
+        for w in ws_:
+            runner = StepRunner(w, states[0], 0, stream)
+            sets = [runner.inputs(t) for t in range(N_INPUT_SETS)]
+            modes = [("cold", states)] if n_rot > 1 else [("hbm", states)]
+            if n_rot > 1:
+                modes.append(("warm", states[:1]))
+            for mode, sts in modes:
+                for st, sv in zip(states, saved):
+                    restore(st, sv)
+                wu = settle_warmup(runner, sts, sets, warmup)
+                for st, sv in zip(states, saved):
+                    restore(st, sv)
+                r = timed_steps(runner, sts, sets, wu, steps)
+                ms_step = r["total_ms"] / steps
+                attn = float(np.mean(r["attn_ms"]))
+                ent = (sum(r["n_before"]) + sum(r["n_after"])) / 2.0 / len(sts) / B
+                nbytes = attn_bytes_per_launch(w, B, ent, 0.0)
+                gbs = nbytes / (attn * 1e-3) / 1e9
+                row = {"point": w.name, "D": w.D, "B": B, "topk": w.topk, "p_agree": w.p_agree, "mode": mode,
+                       "intensity_flop_per_byte": round(4.0 * w.Hq * w.D * w.d * ent * B / nbytes, 1),
+                       "attn_us": round(attn * 1e3, 1),
+                       "attn_us_p10_p50_p90": [round(pct(r["attn_ms"], q) * 1e3, 1) for q in (10, 50, 90)],
+                       "attn_GBps": round(gbs, 1), "attn_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
+                       "attn_frac_of_ceiling": round(gbs / ceiling["GB/s"], 4),
+                       "step_us": round(ms_step * 1e3, 1),
+                       "step_us_p10_p50_p90": [round(pct(r["step_ms"], q) * 1e3, 1) for q in (10, 50, 90)],
+                       "verified_tokens_per_s": round(B * w.D / (ms_step * 1e-3), 1),
+                       "accepted_length": round(r["P_advance"] / B / steps, 3),
+                       "seq_errors": int((runner.err != 0).sum())}
+                if mode != "warm":
+                    row["graph_step_us"] = round(graph_step_ms(runner, sts, sets, steps, states, saved) * 1e3, 1)
+                    row["graph_verified_tokens_per_s"] = round(B * w.D / (row["graph_step_us"] * 1e-6), 1)
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+            del runner, sets
+        del states, saved
+        torch.cuda.empty_cache()
+    write_sweep_table(args, rows, ceiling)
+
+
+def graph_step_ms(runner: StepRunner, sts: list, sets: list, steps: int, states: list, saved: list) -> float:
+    """The same steps captured once in a HIP graph (the calls allocate and synchronise
+    nothing) and replayed: the step time without host launch overhead.  States are
+    restored before the warm-up replay and before the timed one."""
+    import torch
+    import tree_speculative_decoding_amd as tv
+
+    def reset():
+        for st, sv in zip(states, saved):
+            restore(st, sv)
+        torch.cuda.synchronize()
+
+    reset()
+    tv.tv_set_timing_events(None, None)
+    g = torch.cuda.CUDAGraph()
+    eager_stream = runner.stream
+    with torch.cuda.graph(g):
+        runner.stream = torch.cuda.current_stream()
+        for t in range(steps):
+            runner.step(sts[t % len(sts)], sets[t % len(sets)])
+    runner.stream = eager_stream
+    reset()
+    g.replay()
+    reset()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    del g
+    return ms
+
+
+def snapshot(st) -> dict:
+    """Copies of a state's counts, open sums and tail (what a step changes besides pool
+    slots at and beyond n, which are never read until committed again)."""
+    c = lambda xs: [x.clone() for x in xs]
+    return {"P": st.P.clone(), "n": c(st.n), "open_k": c(st.open_k), "open_v": c(st.open_v),
+            "tail": c([t for t in (st.tail_k, st.tail_v) if t is not None])}
+
+
+def restore(st, sv: dict) -> None:
+    st.P.copy_(sv["P"])
+    for dst, src in zip(st.n + st.open_k + st.open_v, sv["n"] + sv["open_k"] + sv["open_v"]):
+        dst.copy_(src)
+    for dst, src in zip([t for t in (st.tail_k, st.tail_v) if t is not None], sv["tail"]):
+        dst.copy_(src)
+
+
+def write_sweep_table(args, rows: list, ceiling: dict) -> None:
+    hdr = ["# Long-context budget sweep: verify step at a 131072-token prefix", "",
+           "64/8 heads, d=128, bf16, 32768 C4 + 1024 C128 committed entries per sequence; one step = plan,",
+           "verify attention with the scratch pad, accept, refresh.  Command (repository root):", "",
+           f"    python3 bench.py --sweep <out.md> --steps {args.steps} --warmup {args.warmup}", "",
+           f"Read ceiling on the same device (plain read-reduce, 4 GiB): {ceiling['GB/s']:.0f} GB/s "
+           f"({100 * ceiling['frac_of_peak']:.1f}% of 8 TB/s).  `cold`: states rotated so each step reads "
+           "its pools from HBM; `warm`: one state back to back (batch 1 and 4 fit the 256 MB last-level "
+           "cache partly or wholly); `hbm`: one state larger than 1 GiB.  Every point first runs untimed "
+           "steps for at least 15 ms.  Attention = the prefix-stream kernel per launch (mean over the timed "
+           "steps, p10 / p90 beside it; the merge kernel of split units is in the step time); intensity = "
+           "attention flops per algorithmic byte; graph = the same steps replayed from one captured HIP "
+           "graph.", "",
+           "| D | B | top-k | p | mode | intensity | attn us (p10-p90) | attn GB/s | % of 8 TB/s | % of ceiling "
+           "| step us | verified tok/s | graph step us | graph tok/s | accepted length |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    body = []
+    for r in sorted(rows, key=lambda r: (r["B"], r["D"], r["topk"], r["p_agree"], r["mode"])):
+        p10, _, p90 = r["attn_us_p10_p50_p90"]
+        body.append(f"| {r['D']} | {r['B']} | {r['topk']} | {r['p_agree']} | {r['mode']} | "
+                    f"{r['intensity_flop_per_byte']} | {r['attn_us']} ({p10}-{p90}) | {r['attn_GBps']:.0f} | "
+                    f"{100 * r['attn_frac_of_peak']:.1f} | {100 * r['attn_frac_of_ceiling']:.1f} | {r['step_us']} | "
+                    f"{r['verified_tokens_per_s']:.0f} | {r.get('graph_step_us', '-')} | "
+                    f"{r.get('graph_verified_tokens_per_s', '-')} | {r['accepted_length']} |")
+    with open(args.sweep, "w") as fh:
+        fh.write("\n".join(hdr + body) + "\n")
 
 
 def time_draft_tree(w, steps: int, stream) -> dict:

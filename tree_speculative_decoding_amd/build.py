@@ -3,7 +3,9 @@
     python -m tree_speculative_decoding_amd.build
 
 Every call recompiles.  Objects go to ``_build/`` next to this file, the shared
-library to ``libtv.so`` in this package directory.
+library to ``libtv.so`` in this package directory.  The measurement aid under
+``measure/`` (a plain HBM read-stream kernel the benchmark reports the ceiling of)
+becomes ``libtv_measure.so``; libtv.so does not contain or need it.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libtv.so")
+MEASURE_OUT = os.path.join(PKG, "libtv_measure.so")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -64,6 +67,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = OUT + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, OUT)
+    msrc = sorted(glob.glob(os.path.join(PKG, "measure", "*.hip")))
+    if msrc:
+        tmp = MEASURE_OUT + ".tmp"
+        _run([cc, *COMMON_FLAGS, "-shared", "-o", tmp, *msrc])
+        os.replace(tmp, MEASURE_OUT)
     return OUT
 
 
