@@ -60,6 +60,9 @@ def parse():
                     help="run the long-context budget sweep instead (D 5..8 x batch 1..64 x top-k 1, 2 at a "
                          "131072-token prefix) and write its table to OUT_MD; one JSON line per point")
     ap.add_argument("--sweep-batches", default="1,4,16,64", help="batch sizes of the sweep (comma-separated)")
+    ap.add_argument("--summarize-sweep-traces", default="", metavar="DIR",
+                    help="write profiles/step_long_context_kernel_trace.md from rocprofv3 kernel-trace csv "
+                         "runs of the sweep, one per batch size, in DIR/b<B>/")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (to scale HBM byte counters)")
     return ap.parse_args()
@@ -107,7 +110,7 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
 
 
-PROFILE_BENCH = "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-extras"
+PROFILE_BENCH = "python3 bench.py --steps 20 --warmup 40 --no-cpu-baseline --no-extras"
 PROFILE_COUNTER_BENCH = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras"
 PREFIX_KERNEL = "tv::k_attn_mfma<4, 1, false>"  # the contiguous-pool instance the benchmark runs
 
@@ -151,7 +154,14 @@ def summarize_profiles(d: str, workload: str) -> None:
         lines.append(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{100.0 * float(r['TotalDurationNs']) / total_ns:.1f}% |")
-    lines += ["", "Bench line of the profiled run:", "", "    " + bench_line, ""]
+    # the timed launches alone (the last `steps` of the prefix kernel), beside the events
+    tr = sorted((r for r in csv.DictReader(open(os.path.join(d, "kt", "run_kernel_trace.csv")))
+                 if PREFIX_KERNEL in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
+    timed = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[-bl["steps"]:]]
+    lines += ["", f"The {len(timed)} timed launches of `{PREFIX_KERNEL}` alone (`run_kernel_trace.csv`): average "
+              f"{sum(timed) / len(timed):.1f} us, against {bl['roofline']['avg_launch_ms'] * 1e3:.1f} us from the HIP "
+              "events of the same launches (the events also hold the dispatch of the kernel).",
+              "", "Bench line of the profiled run:", "", "    " + bench_line, ""]
     open(os.path.join(out_dir, f"attn_prefix_{workload}_kernel_trace.md"), "w").write("\n".join(lines))
 
     fetch = _counter_per_kernel(os.path.join(d, "FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
@@ -166,7 +176,9 @@ def summarize_profiles(d: str, workload: str) -> None:
     pk = [k for k in fetch if PREFIX_KERNEL in k][0]
     rd = fetch[pk] * 1024.0 * fs
     wr = write[pk] * 1024.0 * ws
-    alg = bl["roofline"]["algorithmic_bytes_per_launch"]
+    # algorithmic bytes of the counter runs themselves (their pools are at their own step)
+    fl = json.loads([l for l in open(os.path.join(d, "FETCH_SIZE.txt")).read().splitlines() if l.startswith("{")][-1])
+    alg = fl["roofline"]["algorithmic_bytes_per_launch"]
     cmd = f"rocprofv3 --pmc {{}} --output-format csv -d <dir> -o run -- {PROFILE_COUNTER_BENCH}"
     rec = {"kernel": pk, "workload": workload,
            "command_fetch": cmd.format("FETCH_SIZE"), "command_write": cmd.format("WRITE_SIZE"),
@@ -198,6 +210,35 @@ def summarize_profiles(d: str, workload: str) -> None:
               f"algorithmic: ratio {(rd + wr) / alg:.4f}.", ""]
     open(os.path.join(out_dir, f"hbm_bytes_{workload}.md"), "w").write("\n".join(lines))
     print(json.dumps(rec))
+
+
+SWEEP_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/b{B} -o run -- "
+                   "python3 bench.py --sweep <dir>/b{B}.md --sweep-batches {B} --steps 20 --warmup 5")
+
+
+def summarize_sweep_traces(d: str) -> None:
+    """Per-kernel launch statistics of the sweep's steps at each batch size (one rocprofv3
+    run per batch size, every point of that batch size: D 5..8, top-k 1 and 2, p 0.5 and
+    0.7, cold and warm), as the committed summary."""
+    import csv
+    lines = ["# Kernel-trace summary: the verify step at a 131072-token prefix, by batch size", "",
+             "64/8 heads, d=128, bf16, 32768 C4 + 1024 C128 entries per sequence; every point of the",
+             "long-context sweep at that batch size (D 5..8, top-k 1 and 2, p 0.5 and 0.7; cold and warm",
+             "where the state is under 1 GiB), each with its settling and timed steps.  Commands (repository",
+             "root, TMPDIR=/tmp), one per batch size B:", "", "    " + SWEEP_TRACE_CMD, "",
+             "| B | kernel | calls | average us | min us | max us |", "|---|---|---|---|---|---|"]
+    for sub in sorted(os.listdir(d), key=lambda x: int(x[1:]) if x[1:].isdigit() else 0):
+        path = os.path.join(d, sub, "run_kernel_stats.csv")
+        if not (sub.startswith("b") and sub[1:].isdigit() and os.path.exists(path)):
+            continue
+        for r in csv.DictReader(open(path)):
+            if "tv::" not in r["Name"]:
+                continue
+            lines.append(f"| {sub[1:]} | `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | "
+                         f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                         f"{float(r['MaxNs']) / 1e3:.1f} |")
+    lines.append("")
+    open(os.path.join(ROOT, "profiles", "step_long_context_kernel_trace.md"), "w").write("\n".join(lines))
 
 
 def kernel_source_digest() -> str:
@@ -318,12 +359,12 @@ def timed_steps(runner: StepRunner, states: list, sets: list, warmup: int, steps
     attn_ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
     step_ev = [TimingEvent() for _ in range(steps + 1)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed steps are queued right behind the warm-up (no host synchronisation and no
+    # first-use library kernel in between: an idle GPU restarts the slow first milliseconds)
     for t in range(warmup):
         runner.step(states[t % len(states)], sets[t % len(sets)])
-    torch.cuda.synchronize()
-    n_before = [sum(int(x.sum()) for x in st.n) for st in states]
+    n_dev = [[x.clone() for x in st.n] for st in states]
     P_before = [st.P.clone() for st in states]
-    torch.cuda.synchronize()
     start.record(stream)
     for t in range(steps):
         record(step_ev[t], stream)
@@ -333,6 +374,7 @@ def timed_steps(runner: StepRunner, states: list, sets: list, warmup: int, steps
     stop.record(stream)
     tv.tv_set_timing_events(None, None)
     torch.cuda.synchronize()
+    n_before = [sum(int(x.sum()) for x in nd) for nd in n_dev]
     return {"total_ms": start.elapsed_time(stop),
             "step_ms": [step_ev[t].elapsed_ms(step_ev[t + 1]) for t in range(steps)],
             "attn_ms": [a_.elapsed_ms(b_) for a_, b_ in attn_ev],
@@ -365,6 +407,9 @@ def main():
         return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload)
+        return
+    if args.summarize_sweep_traces:
+        summarize_sweep_traces(args.summarize_sweep_traces)
         return
     if args.sweep:
         sweep(args)
@@ -561,7 +606,7 @@ def sweep(args) -> None:
 def graph_step_ms(runner: StepRunner, sts: list, sets: list, steps: int, states: list, saved: list) -> float:
     """The same steps captured once in a HIP graph (the calls allocate and synchronise
     nothing) and replayed: the step time without host launch overhead.  States are
-    restored before the warm-up replay and before the timed one."""
+    restored before the warm-up replay and (queued behind it) before the timed one."""
     import torch
     import tree_speculative_decoding_amd as tv
 
@@ -580,9 +625,10 @@ def graph_step_ms(runner: StepRunner, sts: list, sets: list, steps: int, states:
             runner.step(sts[t % len(sts)], sets[t % len(sets)])
     runner.stream = eager_stream
     reset()
-    g.replay()
-    reset()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    for st, sv in zip(states, saved):  # queued behind the warm replay: no idle gap
+        restore(st, sv)
     start.record()
     g.replay()
     stop.record()
