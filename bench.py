@@ -292,6 +292,7 @@ class StepRunner:
         import tree_speculative_decoding_amd as tv
         B, D, Hq, Hkv, d, dev = st.B, w.D, w.Hq, w.Hkv, w.d, "cuda"
         self.w, self.parts, self.stream = w, parts, stream
+        self.fused = False  # accept + refresh as one tv_accept_refresh launch
         self.anc = torch.zeros(B, D, dtype=torch.int64, device=dev)
         self.depth = torch.zeros(B, D, dtype=torch.int32, device=dev)
         self.err = torch.zeros(B, dtype=torch.int32, device=dev)
@@ -321,6 +322,10 @@ class StepRunner:
         tv.tv_build_tree_mask(x["parents"], self.anc, self.depth, self.err, s)
         tv.tv_verify_attn(x["q"], x["kt"], x["vt"], self.anc, self.depth, self.err, st, self.sc, self.out, self.lse,
                           self.ws, self.parts, s)
+        if self.fused:
+            tv.tv_accept_refresh(st, self.sc, x["parents"], self.anc, self.depth, x["draft"], x["target"], x["kt"],
+                                 x["vt"], self.m, self.path, self.bonus, self.log, self.err, s)
+            return
         tv.tv_accept(x["parents"], self.anc, self.depth, x["draft"], x["target"], self.err, self.m, self.path,
                      self.bonus, s)
         tv.tv_refresh_state(st, self.sc, x["kt"], x["vt"], self.m, self.path, self.log, self.err, s)
@@ -481,6 +486,17 @@ def main():
         graph_ms = graph_step_ms(runner, [st], sets, args.steps, [st], [saved])
         result["graph_ms_per_step"] = round(graph_ms, 4)
         result["graph_tokens_per_s"] = round(B * D / (graph_ms * 1e-3), 1)
+        # the same steps with acceptance and refresh fused into one launch
+        restore(st, saved)
+        runner.fused = True
+        rf = timed_steps(runner, [st], sets, args.warmup, args.steps)
+        fused_graph_ms = graph_step_ms(runner, [st], sets, args.steps, [st], [saved])
+        runner.fused = False
+        result["fused_accept_refresh"] = {
+            "ms_per_step": round(rf["total_ms"] / args.steps, 4),
+            "graph_ms_per_step": round(fused_graph_ms, 4),
+            "graph_tokens_per_s": round(B * D / (fused_graph_ms * 1e-3), 1),
+            "note": "tv_accept_refresh in place of tv_accept + tv_refresh_state; same steps, same starting state"}
         ceiling = read_ceiling(stream)
         ceiling["attn_frac_of_ceiling"] = round(achieved / ceiling["GB/s"], 4)
         result["read_ceiling"] = ceiling
@@ -595,6 +611,9 @@ def sweep(args) -> None:
                 if mode != "warm":
                     row["graph_step_us"] = round(graph_step_ms(runner, sts, sets, steps, states, saved) * 1e3, 1)
                     row["graph_verified_tokens_per_s"] = round(B * w.D / (row["graph_step_us"] * 1e-6), 1)
+                    runner.fused = True
+                    row["graph_fused_step_us"] = round(graph_step_ms(runner, sts, sets, steps, states, saved) * 1e3, 1)
+                    runner.fused = False
                 rows.append(row)
                 print(json.dumps(row), flush=True)
             del runner, sets
@@ -666,10 +685,10 @@ def write_sweep_table(args, rows: list, ceiling: dict) -> None:
            "steps for at least 15 ms.  Attention = the prefix-stream kernel per launch (mean over the timed "
            "steps, p10 / p90 beside it; the merge kernel of split units is in the step time); intensity = "
            "attention flops per algorithmic byte; graph = the same steps replayed from one captured HIP "
-           "graph.", "",
+           "graph; graph fused = the same with tv_accept_refresh in place of tv_accept + tv_refresh_state.", "",
            "| D | B | top-k | p | mode | intensity | attn us (p10-p90) | attn GB/s | % of 8 TB/s | % of ceiling "
-           "| step us | verified tok/s | graph step us | graph tok/s | accepted length |",
-           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+           "| step us | verified tok/s | graph step us | graph tok/s | graph fused step us | accepted length |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     body = []
     for r in sorted(rows, key=lambda r: (r["B"], r["D"], r["topk"], r["p_agree"], r["mode"])):
         p10, _, p90 = r["attn_us_p10_p50_p90"]
@@ -677,7 +696,8 @@ def write_sweep_table(args, rows: list, ceiling: dict) -> None:
                     f"{r['intensity_flop_per_byte']} | {r['attn_us']} ({p10}-{p90}) | {r['attn_GBps']:.0f} | "
                     f"{100 * r['attn_frac_of_peak']:.1f} | {100 * r['attn_frac_of_ceiling']:.1f} | {r['step_us']} | "
                     f"{r['verified_tokens_per_s']:.0f} | {r.get('graph_step_us', '-')} | "
-                    f"{r.get('graph_verified_tokens_per_s', '-')} | {r['accepted_length']} |")
+                    f"{r.get('graph_verified_tokens_per_s', '-')} | {r.get('graph_fused_step_us', '-')} | "
+                    f"{r['accepted_length']} |")
     with open(args.sweep, "w") as fh:
         fh.write("\n".join(hdr + body) + "\n")
 

@@ -11,6 +11,7 @@
  *   tv_verify_attn       branch-aware causal attention + per-chain scratch  (§3.1, §4.1, §4.2)
  *   tv_accept            accepted-path selection                            (§3.1, §4.4)
  *   tv_refresh_state     accepted-path refresh of the compressed state      (§3.2, §4.2, §4.3)
+ *   tv_accept_refresh    the two calls above in one launch                  (§4.3)
  *
  * plus tv_compress_prefix, which builds the compressed state of a raw prefix.
  *
@@ -57,7 +58,7 @@ extern "C" {
 #define TV_API
 #endif
 
-#define TV_VERSION 110      /* 1.1.0 */
+#define TV_VERSION 111      /* 1.1.1 */
 #define TV_MAX_LEVELS 2
 #define TV_MAX_D 64
 #define TV_POOL_ALIGN 64    /* every pool capacity must be a multiple of this */
@@ -258,6 +259,22 @@ TV_API tv_status tv_refresh_state(int D, const tv_state* st, const tv_scratch* s
                                   const void* k_tree, const void* v_tree, const int32_t* m,
                                   const int32_t* path, int32_t* commit_log, int32_t* seq_err,
                                   hipStream_t stream);
+
+/*
+ * tv_accept followed by tv_refresh_state in one launch (TSD-V4 §4.3: keeping the
+ * refresh cheap; on this path its cost is launch and round-trip latency, not bytes).
+ * One workgroup per sequence: its first wave selects the accepted path into on-chip
+ * memory and the workgroup refreshes from it, so m and the path are not read back.
+ * Arguments as for the two calls (B = st->B); m, path and bonus are written as
+ * tv_accept writes them, the state, commit_log and seq_err as tv_refresh_state does.
+ * Results are identical to the two calls made in order.
+ */
+TV_API tv_status tv_accept_refresh(int D, const tv_state* st, const tv_scratch* scratch,
+                                   const int32_t* parents, const uint64_t* anc, const int32_t* depth,
+                                   const int32_t* draft_tok, const int32_t* target_tok,
+                                   const void* k_tree, const void* v_tree, int32_t* m, int32_t* path,
+                                   int32_t* bonus, int32_t* commit_log, int32_t* seq_err,
+                                   hipStream_t stream);
 
 /*
  * Compressed state of a raw committed prefix (TSD-V4 §2.2: compression along the

@@ -163,11 +163,19 @@ class Runner:
         import tree_speculative_decoding_amd as tv
         tv.tv_refresh_state(self.st, self.sc, x.kt, x.vt, self.m, self.path, self.log, self.err)
 
-    def step(self, x: DevStep):
+    def accept_refresh(self, x: DevStep):
+        import tree_speculative_decoding_amd as tv
+        tv.tv_accept_refresh(self.st, self.sc, x.parents, self.anc, self.depth, x.draft, x.target, x.kt, x.vt,
+                             self.m, self.path, self.bonus, self.log, self.err)
+
+    def step(self, x: DevStep, fused: bool = False):
         self.plan(x)
         self.attend(x)
-        self.accept(x)
-        self.refresh(x)
+        if fused:
+            self.accept_refresh(x)
+        else:
+            self.accept(x)
+            self.refresh(x)
 
 
 def _tdt(dtype):

@@ -15,7 +15,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert tv.tv_version() == 110
+    assert tv.tv_version() == 111
 
 
 def test_struct_layout_matches_header():
@@ -105,6 +105,20 @@ def test_refresh_and_compress_reject_bad_args():
     assert L.tv_compress_prefix(ctypes.byref(s), P, P, -1, P, None) == tv.TV_EINVAL
     assert L.tv_compress_prefix(ctypes.byref(s), None, P, 10, P, None) == tv.TV_EINVAL
     assert L.tv_set_timing_events(P, None) == tv.TV_EINVAL
+
+
+def test_accept_refresh_rejects_bad_args():
+    L = tv.lib()
+    s = fake_state()
+    sc = TvScratch()
+    args = [P] * 12 + [None]  # parents .. seq_err, stream
+    assert L.tv_accept_refresh(8, ctypes.byref(s), None, *args) == tv.TV_EINVAL  # no scratch
+    assert L.tv_accept_refresh(8, ctypes.byref(s), ctypes.byref(sc), *args) == tv.TV_EINVAL  # NULL scratch levels
+    assert L.tv_accept_refresh(0, ctypes.byref(s), ctypes.byref(sc), *args) == tv.TV_EINVAL  # D < 1
+    assert L.tv_accept_refresh(65, ctypes.byref(s), ctypes.byref(sc), *args) == tv.TV_EINVAL  # D > 64
+    nulls = [P] * 12
+    nulls[4] = None  # target tokens
+    assert L.tv_accept_refresh(8, ctypes.byref(s), ctypes.byref(sc), *nulls, None) == tv.TV_EINVAL
 
 
 def test_status_strings():

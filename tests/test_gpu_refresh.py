@@ -137,3 +137,82 @@ def test_pool_full_leaves_sequence_unchanged():
         assert torch.equal(dst.pool_k[0][b], before[2][b])
         assert torch.equal(dst.open_k[0][b], before[3][b])
         assert torch.equal(dst.tail_k[b], before[4][b])
+
+
+FUSED = {
+    "bf16_c4_c128": (synth.Workload("fu1", 4, 8, 16, 2, 128, "bf16", (4, 128), 122, 2, 3, 0.8, 3301, prefix="raw"), 40),
+    "f32_d64_c4_c16": (synth.Workload("fu2", 3, 7, 8, 2, 64, "f32", (4, 16), 13, 2, 3, 0.6, 3302, prefix="raw"), 30),
+    "bf16_chain_c1_c4": (synth.Workload("fu3", 2, 8, 8, 1, 128, "bf16", (1, 4), 9, 1, 7, 0.9, 3303, prefix="raw"), 25),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_accept_refresh_equals_separate_calls(name):
+    """tv_accept_refresh against tv_accept + tv_refresh_state on two copies of the same
+    state, step after step: m, path, bonus, commit log, status and every byte of the state
+    identical; the fused run also against the oracle."""
+    import torch
+    w, T = FUSED[name]
+    _say(f"fused accept+refresh {name}: {T} steps")
+    caps = pooled_caps(w, T * w.D + 8)
+    sep, fus = device_state(w, caps, poison=True), device_state(w, caps, poison=True)
+    ost = oracle_state(w, caps)
+    rs, rf = Runner(sep, w.D, w.Hq), Runner(fus, w.D, w.Hq)
+    for t in range(T):
+        s = synth.step_inputs(w, t)
+        h = widen_step(s, w.dtype)
+        rs.step(upload_step(s, w.dtype))
+        rf.step(upload_step(s, w.dtype), fused=True)
+        torch.cuda.synchronize()
+        for a, b in ((rs.m, rf.m), (rs.path, rf.path), (rs.bonus, rf.bonus), (rs.log, rf.log), (rs.err, rf.err)):
+            assert torch.equal(a, b), f"step {t}"
+        _same_state(sep, fus, w)
+        ref = oracle.step(ost, s.parents, s.draft, s.target, h.q, h.kt, h.vt)
+        assert (rf.m.cpu().numpy() == ref.m).all() and (rf.path.cpu().numpy() == ref.path).all()
+        assert (rf.log.cpu().numpy()[:, :len(w.levels)] == ref.commit_log).all()
+        ost = ref.state
+        compare_state(fus, ost, w.dtype, f"fused step {t}")
+
+
+def _same_state(a, b, w):
+    import torch
+
+    def bits(x):
+        return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+    assert torch.equal(a.P, b.P)
+    for l in range(len(w.levels)):
+        assert torch.equal(a.n[l], b.n[l])
+        assert torch.equal(bits(a.pool_k[l]), bits(b.pool_k[l]))
+        assert torch.equal(bits(a.pool_vt[l]), bits(b.pool_vt[l]))
+        assert torch.equal(a.open_k[l], b.open_k[l]) and torch.equal(a.open_v[l], b.open_v[l])
+    if a.tail_k is not None:
+        assert torch.equal(bits(a.tail_k), bits(b.tail_k)) and torch.equal(bits(a.tail_v), bits(b.tail_v))
+
+
+def test_fused_accept_refresh_flagged_and_full_sequences():
+    """Sequences flagged before acceptance (a bad parent array) and sequences whose pool
+    would overflow: the fused call leaves them exactly as the two separate calls do."""
+    import torch
+    import tree_speculative_decoding_amd as tv
+    _say("fused accept+refresh: flagged and full sequences")
+    w = synth.Workload("fuf", 4, 8, 8, 1, 64, "f32", (4,), 60, 1, 7, 1.0, 3310, prefix="raw")
+    runs = []
+    for fused in (False, True):
+        dst = device_state(w, [64])
+        dst.P.copy_(torch.tensor([60, 252, 40, 100], dtype=torch.int32))
+        rk = np.stack([synth.raw_prefix(w, b, 255)[0] for b in range(w.B)])
+        err = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+        tv.tv_compress_prefix(dst, tv.to_device(rk, "f32"), tv.to_device(rk, "f32"), err)
+        s = synth.step_inputs(w, 0)
+        x = upload_step(s, w.dtype)
+        x.parents[2, 5] = 7  # a parent after its child: sequence 2 is flagged by the plan
+        r = Runner(dst, w.D, w.Hq)
+        r.step(x, fused=fused)
+        torch.cuda.synchronize()
+        runs.append((r, dst))
+    (rs, sep), (rf, fus) = runs
+    assert rs.err.cpu().numpy().tolist() == [0, tv.TV_SEQ_POOL_FULL, tv.TV_SEQ_BAD_PARENT, 0]
+    for a, b in ((rs.m, rf.m), (rs.path, rf.path), (rs.bonus, rf.bonus), (rs.log, rf.log), (rs.err, rf.err)):
+        assert torch.equal(a, b)
+    _same_state(sep, fus, w)

@@ -12,38 +12,22 @@
 // path leaf's open-block sums replace the open sums, path tokens extend the raw
 // tail.  Counters (P, n) are written after a barrier, once every thread of the
 // sequence has read the old values.  Rejected nodes are never read.
+#include "accept_path.h"
 #include "tv_launch.h"
 
 namespace tv {
 
+// The refresh of sequence b once its accepted path is in LDS (pth[0..m], m < D checked
+// by the caller's path validation into path_bad) and every thread has read the old
+// counters: P is sequence b's committed length before the refresh.
 template <typename T>
-__global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch sc,
-                                                  const T* __restrict__ k_tree,
-                                                  const T* __restrict__ v_tree,
-                                                  const int32_t* __restrict__ m_in,
-                                                  const int32_t* __restrict__ path,
-                                                  int32_t* __restrict__ commit_log,
-                                                  int32_t* __restrict__ seq_err) {
-  __shared__ int pth[TV_MAX_D];
-  __shared__ int path_bad;
-  const int b = blockIdx.x;
+__device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, const tv_scratch& sc,
+                                             const T* __restrict__ k_tree, const T* __restrict__ v_tree, int m,
+                                             int P, const int* pth, bool path_bad, int32_t* __restrict__ commit_log,
+                                             int32_t* __restrict__ seq_err) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int L = st.n_levels;
   const int Hkv = st.Hkv, d = st.d, HD = Hkv * d;
-  if (commit_log != nullptr)
-    for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
-  const int err = seq_err[b];
-  const int m = m_in[b];
-  const int P = st.P[b];
-  if (tid == 0) path_bad = 0;
-  __syncthreads();  // log prefill and the reads above happen before any later write
-  if (err != TV_SEQ_OK || m < 0) return;
-  if (tid < D) {
-    const int v = path[(size_t)b * D + tid];
-    pth[tid] = v;
-    if (tid <= m && (v < 0 || v >= D)) atomicOr(&path_bad, 1);
-  }
-  __syncthreads();
   if (m >= D || P < 0 || path_bad) {
     if (tid == 0) seq_err[b] = TV_SEQ_BAD_PATH;
     return;
@@ -121,6 +105,98 @@ __global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch
     st.P[b] = P2;
     for (int l = 0; l < L; ++l) st.lvl[l].n[b] = P2 / st.lvl[l].C;
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch sc,
+                                                  const T* __restrict__ k_tree,
+                                                  const T* __restrict__ v_tree,
+                                                  const int32_t* __restrict__ m_in,
+                                                  const int32_t* __restrict__ path,
+                                                  int32_t* __restrict__ commit_log,
+                                                  int32_t* __restrict__ seq_err) {
+  __shared__ int pth[TV_MAX_D];
+  __shared__ int path_bad;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int L = st.n_levels;
+  if (commit_log != nullptr)
+    for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
+  const int err = seq_err[b];
+  const int m = m_in[b];
+  const int P = st.P[b];
+  if (tid == 0) path_bad = 0;
+  __syncthreads();  // log prefill and the reads above happen before any later write
+  if (err != TV_SEQ_OK || m < 0) return;
+  if (tid < D) {
+    const int v = path[(size_t)b * D + tid];
+    pth[tid] = v;
+    if (tid <= m && (v < 0 || v >= D)) atomicOr(&path_bad, 1);
+  }
+  __syncthreads();
+  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, pth, path_bad != 0, commit_log, seq_err);
+}
+
+// Acceptance and refresh in one launch (one workgroup per sequence): the first wave
+// selects the accepted path into LDS (and writes m, path and bonus as tv_accept does),
+// then the workgroup refreshes from it.  Saves a launch and the round trip that reads m
+// and the path back; results are those of tv_accept followed by tv_refresh_state.
+template <typename T>
+__global__ __launch_bounds__(1024) void k_accept_refresh(int D, tv_state st, tv_scratch sc,
+                                                         const int32_t* __restrict__ parents,
+                                                         const uint64_t* __restrict__ anc,
+                                                         const int32_t* __restrict__ depth,
+                                                         const int32_t* __restrict__ draft,
+                                                         const int32_t* __restrict__ target,
+                                                         const T* __restrict__ k_tree,
+                                                         const T* __restrict__ v_tree,
+                                                         int32_t* __restrict__ m_out, int32_t* __restrict__ path,
+                                                         int32_t* __restrict__ bonus,
+                                                         int32_t* __restrict__ commit_log,
+                                                         int32_t* __restrict__ seq_err) {
+  __shared__ int pth[TV_MAX_D];
+  __shared__ int m_s;
+  __shared__ int path_bad;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int L = st.n_levels;
+  if (commit_log != nullptr)
+    for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
+  const int err = seq_err[b];
+  const int P = st.P[b];
+  if (tid < 64) {  // the first wave: every path slot -1, then the accepted path
+    if (tid < D) pth[tid] = -1;
+    const int m = accept_one(b, D, parents, anc, depth, draft, target, err, m_out, path, bonus, pth);
+    if (tid == 0) {
+      m_s = m;
+      path_bad = 0;
+    }
+  }
+  __syncthreads();  // the path is in LDS; the log prefill and the reads above are done
+  const int m = m_s;
+  if (err != TV_SEQ_OK || m < 0) return;
+  // slots 0..m hold one node each for a plan from tv_build_tree_mask; checked as
+  // tv_refresh_state checks a path it is given
+  if (tid < D && tid <= m && (pth[tid] < 0 || pth[tid] >= D)) atomicOr(&path_bad, 1);
+  __syncthreads();
+  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, pth, path_bad != 0, commit_log, seq_err);
+}
+
+hipError_t launch_accept_refresh(int D, const tv_state& st, const tv_scratch& sc, const int32_t* parents,
+                                 const uint64_t* anc, const int32_t* depth, const int32_t* draft,
+                                 const int32_t* target, const void* k_tree, const void* v_tree, int32_t* m,
+                                 int32_t* path, int32_t* bonus, int32_t* commit_log, int32_t* seq_err,
+                                 hipStream_t s) {
+  if (st.B == 0) return hipSuccess;
+  dim3 grid(st.B), block(st.Hkv * st.d >= 1024 ? 1024 : ((st.Hkv * st.d + 63) / 64) * 64);
+  if (st.dtype == TV_BF16)
+    hipLaunchKernelGGL(k_accept_refresh<uint16_t>, grid, block, 0, s, D, st, sc, parents, anc, depth, draft,
+                       target, (const uint16_t*)k_tree, (const uint16_t*)v_tree, m, path, bonus, commit_log,
+                       seq_err);
+  else
+    hipLaunchKernelGGL(k_accept_refresh<float>, grid, block, 0, s, D, st, sc, parents, anc, depth, draft, target,
+                       (const float*)k_tree, (const float*)v_tree, m, path, bonus, commit_log, seq_err);
+  return hipGetLastError();
 }
 
 hipError_t launch_refresh(int D, const tv_state& st, const tv_scratch& sc, const void* k_tree,

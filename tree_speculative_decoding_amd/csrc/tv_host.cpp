@@ -334,6 +334,31 @@ TV_API tv_status tv_refresh_state(int D, const tv_state* st, const tv_scratch* s
                    "refresh launch");
 }
 
+TV_API tv_status tv_accept_refresh(int D, const tv_state* st, const tv_scratch* scratch, const int32_t* parents,
+                                   const uint64_t* anc, const int32_t* depth, const int32_t* draft_tok,
+                                   const int32_t* target_tok, const void* k_tree, const void* v_tree, int32_t* m,
+                                   int32_t* path, int32_t* bonus, int32_t* commit_log, int32_t* seq_err,
+                                   hipStream_t stream) {
+  tv_status s = check_state(st);
+  if (s != TV_OK) return s;
+  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
+  if (st->B == 0) return ok();
+  if (!parents || !anc || !depth || !draft_tok || !target_tok || !k_tree || !v_tree || !m || !path || !bonus ||
+      !seq_err)
+    return fail(TV_EINVAL, "NULL pointer argument");
+  tv_scratch sc{};
+  if (st->n_levels > 0) {
+    if (scratch == nullptr) return fail(TV_EINVAL, "scratch is NULL");
+    for (int l = 0; l < st->n_levels; ++l)
+      if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
+        return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
+    sc = *scratch;
+  }
+  return hip_check(tv::launch_accept_refresh(D, *st, sc, parents, anc, depth, draft_tok, target_tok, k_tree, v_tree,
+                                             m, path, bonus, commit_log, seq_err, stream),
+                   "accept + refresh launch");
+}
+
 TV_API tv_status tv_compress_prefix(const tv_state* st, const void* raw_k, const void* raw_v, int max_len,
                                     int32_t* seq_err, hipStream_t stream) {
   tv_status s = check_state(st);

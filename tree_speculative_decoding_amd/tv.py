@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
             "tv_accept": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
             "tv_refresh_state": ([i32, ctypes.POINTER(TvState), ctypes.POINTER(TvScratch), vp, vp, vp,
                                   vp, vp, vp, vp], i32),
+            "tv_accept_refresh": ([i32, ctypes.POINTER(TvState), ctypes.POINTER(TvScratch), vp, vp, vp, vp, vp,
+                                   vp, vp, vp, vp, vp, vp, vp, vp], i32),
             "tv_compress_prefix": ([ctypes.POINTER(TvState), vp, vp, i32, vp, vp], i32),
             "tv_set_timing_events": ([vp, vp], i32),
             "tv_build_draft_tree": ([i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
@@ -369,6 +371,18 @@ def tv_refresh_state(st, scratch, k_tree, v_tree, m, path, commit_log, seq_err, 
     _check(lib().tv_refresh_state(D, ctypes.byref(s), ctypes.byref(sc) if sc is not None else None,
                                   _ptr(k_tree), _ptr(v_tree), _ptr(m), _ptr(path), _ptr(commit_log),
                                   _ptr(seq_err), _stream(stream)))
+
+
+def tv_accept_refresh(st, scratch, parents, anc, depth, draft_tok, target_tok, k_tree, v_tree, m, path, bonus,
+                      commit_log, seq_err, stream=None) -> None:
+    """tv_accept followed by tv_refresh_state, in one launch."""
+    D = k_tree.shape[1]
+    s = _state(st)
+    sc = _scratch(scratch)
+    _check(lib().tv_accept_refresh(D, ctypes.byref(s), ctypes.byref(sc) if sc is not None else None,
+                                   _ptr(parents), _ptr(anc), _ptr(depth), _ptr(draft_tok), _ptr(target_tok),
+                                   _ptr(k_tree), _ptr(v_tree), _ptr(m), _ptr(path), _ptr(bonus), _ptr(commit_log),
+                                   _ptr(seq_err), _stream(stream)))
 
 
 def tv_compress_prefix(st, raw_k: torch.Tensor, raw_v: torch.Tensor, seq_err: torch.Tensor,
