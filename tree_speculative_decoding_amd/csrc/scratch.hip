@@ -49,12 +49,19 @@ __global__ __launch_bounds__(256) void k_scratch(AttnArgs a) {
   const int b = blockIdx.x / a.D;
   const int i = blockIdx.x - b * a.D;
   const int tid = threadIdx.x;
-  if (tid < a.D) dep_s[tid] = a.depth[(size_t)b * a.anc_ld + tid];
-  __syncthreads();
-  if (a.seq_err != nullptr && a.seq_err[b] != TV_SEQ_OK) return;  // uniform
-
+  // every load that needs no other load's result goes out in one round trip (issued by
+  // every lane, without branches): the depths, the status, P, the node's chain
+  const int dval = a.depth[(size_t)b * a.anc_ld + (tid < a.D ? tid : 0)];
+  const int eval = *(a.seq_err != nullptr ? a.seq_err + b : a.P + b);
   const int P = a.P[b];
   const uint64_t chain = a.anc[(size_t)b * a.anc_ld + i] & node_mask(a.D);
+  // (an empty use of all four: the compiler issues them together and waits once, instead
+  // of moving each load down to its first use)
+  asm volatile("" ::"v"(dval), "v"(eval), "v"(P), "v"((uint32_t)chain), "v"((uint32_t)(chain >> 32)));
+  if (tid < a.D) dep_s[tid] = dval;
+  __syncthreads();
+  if (a.seq_err != nullptr && eval != TV_SEQ_OK) return;  // uniform
+
   const int pos = P + dep_s[i];
   int b0[TV_MAX_LEVELS];
 #pragma unroll
