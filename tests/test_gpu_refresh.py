@@ -118,7 +118,7 @@ def test_pool_full_leaves_sequence_unchanged():
     err = torch.zeros(w.B, dtype=torch.int32, device="cuda")
     tv.tv_compress_prefix(dst, tv.to_device(rk, "f32"), tv.to_device(rk, "f32"), err)
     torch.cuda.synchronize()
-    before = [t.clone() for t in (dst.P, dst.n[0], dst.pool_k[0], dst.open_k[0], dst.tail_k)]
+    before = [t.clone() for t in (dst.P, dst.n[0], dst.logical_k(0), dst.open_k[0], dst.tail_k)]
     r = Runner(dst, w.D, w.Hq)
     s = synth.step_inputs(w, 0)
     x = upload_step(s, w.dtype)
@@ -134,7 +134,7 @@ def test_pool_full_leaves_sequence_unchanged():
     for b in (1, 2):
         assert P[b] == before[0][b].item()
         assert dst.n[0][b].item() == before[1][b].item()
-        assert torch.equal(dst.pool_k[0][b], before[2][b])
+        assert torch.equal(dst.logical_k(0)[b], before[2][b])
         assert torch.equal(dst.open_k[0][b], before[3][b])
         assert torch.equal(dst.tail_k[b], before[4][b])
 

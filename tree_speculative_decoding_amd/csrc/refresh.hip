@@ -52,7 +52,7 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
   }
   const int leaf = pth[m];
   for (int l = 0; l < L; ++l) {
-    const int C = st.lvl[l].C, cap = st.lvl[l].cap;
+    const int C = st.lvl[l].C;
     T* pk = (T*)st.lvl[l].k;
     T* pvt = (T*)st.lvl[l].vt;
     const T* ek = (const T*)sc.entry_k[l];
@@ -65,7 +65,7 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
       for (int e = tid; e < HD; e += nt) {
         const int g = e / d, dd = e - g * d;
         const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
-        const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, Hkv, cap, d, b, g, j >> 6);
+        const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, st.B, Hkv, d, b, g, j >> 6);
         pk[tb + (size_t)(j & 63) * d + dd] = ek[src];
         pvt[tb + (size_t)dd * 64 + (j & 63)] = ev[src];
       }

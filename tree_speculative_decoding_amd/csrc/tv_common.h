@@ -53,11 +53,14 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 }
 
 // Element offset of tile t (entries 64t .. 64t+63) of (sequence b, KV head g) in a
-// level's K or V^T pool (both hold 64*d elements per tile): contiguous pools by (b, g, t),
-// paged pools by the physical page `page` (the caller reads page_table[b][t]).
-__device__ __forceinline__ size_t tile_offset(bool paged, int page, int Hkv, int cap, int d, int b, int g,
-                                              int t) {
-  return paged ? ((size_t)page * Hkv + g) * 64 * d : (((size_t)b * Hkv + g) * cap + (size_t)t * 64) * d;
+// level's K or V^T pool (both hold 64*d elements per tile).  Tiles are grouped by
+// (tile, sequence) in groups of the Hkv heads' tiles: a paged pool takes the group's
+// place from the page table (the caller reads page_table[b][t]); a contiguous pool puts
+// group (t, b) at t*B + b, so tile t of every sequence lies side by side and the
+// streams that read all sequences' prefixes at once stay within one window of memory.
+__device__ __forceinline__ size_t tile_offset(bool paged, int page, int B, int Hkv, int d, int b, int g, int t) {
+  const size_t group = paged ? (size_t)page : (size_t)t * B + b;
+  return (group * Hkv + g) * 64 * d;
 }
 
 // Physical page of tile t of sequence b in a level (0 for a contiguous pool); false if the

@@ -167,6 +167,10 @@ class DeviceState:
     """Device tensors of a tv_state: pools (K row-major, V transposed), counts, open
     sums, tail and committed lengths.  Allocation and data movement only; no arithmetic.
 
+    Contiguous pools are [cap/64][B][Hkv][64][d] (K) and [cap/64][B][Hkv][d][64] (V^T):
+    tile t of every sequence side by side; logical_k / logical_vt give the per-sequence
+    views.
+
     With ``page_seed`` set the pools are paged: each level holds B * cap/64 (+ ``spare_pages``)
     physical pages of 64 entries for all KV heads, and a page table maps every
     sequence's 64-entry tiles to a random permutation of them."""
@@ -194,10 +198,10 @@ class DeviceState:
                 self.num_pages.append(npg)
                 self.pool_k.append(z(npg, Hkv, A, d))
                 self.pool_vt.append(z(npg, Hkv, d, A))
-        else:
+        else:  # tile t of every sequence side by side: [cap/64][B][Hkv][...]
             self.page_table, self.num_pages = None, None
-            self.pool_k = [z(B, Hkv, c, d) for c in self.caps]
-            self.pool_vt = [z(B, Hkv, c // A, d, A) for c in self.caps]
+            self.pool_k = [z(c // A, B, Hkv, A, d) for c in self.caps]
+            self.pool_vt = [z(c // A, B, Hkv, d, A) for c in self.caps]
         self.n = [z(B, dt=torch.int32) for _ in self.levels]
         self.open_k = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
         self.open_v = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
@@ -238,9 +242,13 @@ class DeviceState:
         [Hkv][cap/64][d][64] (tile_vt); both of the state's element type."""
         A = TV_POOL_ALIGN
         n = k.shape[1]
-        if not self.paged:
-            self.pool_k[l][b, :, :n] = k
-            self.pool_vt[l][b] = vt
+        if not self.paged:  # K: only entries < n are written; V^T: whole tiles
+            full, r = n // A, n % A
+            if full:
+                self.pool_k[l][:full, b] = k[:, :full * A].reshape(self.Hkv, full, A, self.d).permute(1, 0, 2, 3)
+            if r:
+                self.pool_k[l][full, b, :, :r] = k[:, full * A:n]
+            self.pool_vt[l][:, b] = vt.permute(1, 0, 2, 3)
             return
         pps = self.caps[l] // A
         pages = self.page_table[l][b].long()
@@ -250,17 +258,18 @@ class DeviceState:
         self.pool_vt[l][pages] = vt.permute(1, 0, 2, 3)
 
     def logical_k(self, l: int) -> torch.Tensor:
-        """Level l's K pool as [B][Hkv][cap][d] (a gather for a paged pool)."""
+        """Level l's K pool as [B][Hkv][cap][d] (a copy)."""
         if not self.paged:
-            return self.pool_k[l]
+            return self.pool_k[l].permute(1, 2, 0, 3, 4).reshape(self.B, self.Hkv, self.caps[l], self.d)
         A = TV_POOL_ALIGN
         g = self.pool_k[l][self.page_table[l].long()]  # [B][pps][Hkv][64][d]
         return g.permute(0, 2, 1, 3, 4).reshape(self.B, self.Hkv, self.caps[l], self.d)
 
     def logical_vt(self, l: int) -> torch.Tensor:
-        """Level l's V tiles as [B][Hkv][cap/64][d][64] (a gather for a paged pool)."""
+        """Level l's V tiles as [B][Hkv][cap/64][d][64] (a view of a contiguous pool, a
+        gather of a paged one)."""
         if not self.paged:
-            return self.pool_vt[l]
+            return self.pool_vt[l].permute(1, 2, 0, 3, 4)
         g = self.pool_vt[l][self.page_table[l].long()]  # [B][pps][Hkv][d][64]
         return g.permute(0, 2, 1, 3, 4)
 
