@@ -58,9 +58,10 @@ extern "C" {
 #define TV_API
 #endif
 
-#define TV_VERSION 120      /* 1.2.0: contiguous pools grouped by tile */
+#define TV_VERSION 120      /* 1.2.0: contiguous pools in runs of TV_TILE_RUN tiles */
 #define TV_MAX_LEVELS 2
 #define TV_MAX_D 64
+#define TV_TILE_RUN 16     /* tiles of one (sequence, KV head) kept together in a contiguous pool */
 #define TV_POOL_ALIGN 64    /* every pool capacity must be a multiple of this */
 #define TV_DT_MAX_CAND 2048 /* candidates of an expanded draft tree (tv_build_draft_tree) */
 
@@ -87,12 +88,14 @@ enum {
 /* One compression level (the pages' C4 / C128 compressed states, TSD-V4 §2.2, §4.3).
  * A level's entries live in 64-entry tiles (TV_POOL_ALIGN): tile t of (sequence b, KV
  * head g) holds entries 64t .. 64t+63, as 64 rows of d (K) and as d rows of 64 (V,
- * transposed inside the tile); the Hkv heads' tiles of one (sequence, 64 entries) form a
- * group.  Contiguous pool (page_table == NULL): group (t, b) is group t*B + b, i.e. k is
- * [cap/64][B][Hkv][64][d] and vt [cap/64][B][Hkv][d][64], tile t of every sequence side by
- * side (a step reads every sequence's prefix at once, and this keeps those reads within
- * one window of memory instead of at a large fixed stride).  Paged pool (TSD-V4 §4.2: a page-based pool
- * whose pages are referenced by pointers): k and vt hold num_pages physical pages, each
+ * transposed inside the tile).  Contiguous pool (page_table == NULL), T = cap/64 tiles per
+ * (b, g), R = TV_TILE_RUN: for q < floor(T/R), tiles R*q .. R*q+R-1 of (b, g) are tiles
+ * ((q*B + b)*Hkv + g)*R + 0 .. R-1 of k and vt; the last T mod R tiles of (b, g) are tiles
+ * floor(T/R)*B*Hkv*R + (b*Hkv + g)*(T mod R) + 0 ..  (k: [B*Hkv*T][64][d] tiles, vt:
+ * [B*Hkv*T][d][64]).  A step reads every sequence's prefix at once; this keeps those reads
+ * within one window of memory instead of at a fixed stride of one sequence's pool.
+ * Paged pool (TSD-V4 §4.2: a page-based pool whose pages are referenced by pointers):
+ * k and vt hold num_pages physical pages, each
  * the tiles of all Hkv heads for 64 entries ([num_pages][Hkv][64][d] and
  * [num_pages][Hkv][d][64]); page_table[b][t] is the physical page of sequence b's
  * entries 64t .. 64t+63, and cap = 64 * pages_per_seq.  Page ids outside
@@ -101,8 +104,8 @@ enum {
 typedef struct {
   int32_t C;        /* block size: tokens per compressed entry (>= 1) */
   int32_t cap;      /* capacity in entries, a multiple of TV_POOL_ALIGN */
-  void* k;          /* contiguous: [cap/64][B][Hkv][64][d]; paged: [num_pages][Hkv][64][d] */
-  void* vt;         /* contiguous: [cap/64][B][Hkv][d][64]; paged: [num_pages][Hkv][d][64] */
+  void* k;          /* contiguous: B*Hkv*cap/64 tiles [64][d] (see above); paged: [num_pages][Hkv][64][d] */
+  void* vt;         /* contiguous: B*Hkv*cap/64 tiles [d][64]; paged: [num_pages][Hkv][d][64] */
   int32_t* n;       /* [B] committed entries of each sequence (kept equal to P/C) */
   float* open_k;    /* [B][Hkv][d] fp32 sum of the committed tokens of the open block */
   float* open_v;    /* [B][Hkv][d] */

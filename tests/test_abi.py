@@ -140,3 +140,23 @@ def test_draft_tree_rejects_bad_sizes():
     assert f(2, 8, 3, 8, 4, P, P, P, P, None, None) == tv.TV_EINVAL          # vocab < topk
     assert f(2, 2, 3, 8, 1024, None, P, P, P, None, None) == tv.TV_EINVAL    # NULL logits
     assert f(0, 2, 3, 8, 1024, None, None, None, None, None, None) == tv.TV_OK  # B = 0
+
+
+@pytest.mark.parametrize("B,Hkv,cap", [(1, 1, 64), (3, 2, 640), (2, 8, 1024), (64, 8, 8384), (5, 3, 2112), (4, 8, 33792)])
+def test_contiguous_tile_index_is_a_permutation_with_runs(B, Hkv, cap):
+    """The contiguous pool layout (include/tv.h): every (sequence, head, tile) has its own
+    tile, all B*Hkv*cap/64 tiles are used, tiles within a run of TV_TILE_RUN are
+    consecutive, and tile t of every (b, g) lies in the same window for complete runs."""
+    import numpy as np
+    from tree_speculative_decoding_amd.tv import TV_TILE_RUN, contiguous_tile_index
+    idx = contiguous_tile_index(B, Hkv, cap)
+    T = cap // 64
+    assert idx.shape == (B, Hkv, T)
+    assert np.array_equal(np.sort(idx.reshape(-1)), np.arange(B * Hkv * T))
+    R, full = TV_TILE_RUN, T // TV_TILE_RUN
+    for t in range(T):
+        if t % R and (t // R < full or t >= full * R):
+            assert (idx[:, :, t] == idx[:, :, t - 1] + 1).all()  # runs (and the last tiles) are consecutive
+    for q in range(full):  # run range q of every (b, g): one window of B*Hkv*R tiles
+        w = idx[:, :, q * R:(q + 1) * R]
+        assert w.min() == q * B * Hkv * R and w.max() == (q + 1) * B * Hkv * R - 1

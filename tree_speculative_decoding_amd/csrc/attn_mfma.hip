@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
         int lvl, e0, cnt;
         chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
         if (!PAGED || (pid >= 0 && pid < (lvl == 0 ? a.npages[0] : a.npages[1]))) {
-          const size_t off = tile_offset(PAGED, pid, a.B, a.Hkv, kDH, b, g, e0 >> 6) * 2;
+          const size_t off = tile_offset(PAGED, pid, a.cap[lvl], a.B, a.Hkv, kDH, b, g, e0 >> 6) * 2;
           kb = (const char*)a.pk[lvl] + off;   // K rows
           vb = (const char*)a.pvt[lvl] + off;  // V^T tile
         }

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
       const int tile = e0 >> 6;
       const int page = paged ? a.pt[lvl][(size_t)b * a.ppseq[lvl] + tile] : 0;
       const bool page_ok = !paged || (page >= 0 && page < a.npages[lvl]);
-      const size_t tb = tile_offset(paged, page, a.B, a.Hkv, DH, b, g, tile);
+      const size_t tb = tile_offset(paged, page, a.cap[lvl], a.B, a.Hkv, DH, b, g, tile);
       for (int sub = 0; sub * TK < cnt; ++sub) {
         const int base = e0 + sub * TK;
         const int n_sub = min(TK, cnt - sub * TK);

@@ -65,7 +65,7 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
       for (int e = tid; e < HD; e += nt) {
         const int g = e / d, dd = e - g * d;
         const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
-        const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, st.B, Hkv, d, b, g, j >> 6);
+        const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, st.lvl[l].cap, st.B, Hkv, d, b, g, j >> 6);
         pk[tb + (size_t)(j & 63) * d + dd] = ek[src];
         pvt[tb + (size_t)dd * 64 + (j & 63)] = ev[src];
       }

@@ -52,15 +52,31 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Tiles of one (sequence, KV head) that a contiguous pool keeps next to each other.
+constexpr int kTileRun = 16;
+
 // Element offset of tile t (entries 64t .. 64t+63) of (sequence b, KV head g) in a
-// level's K or V^T pool (both hold 64*d elements per tile).  Tiles are grouped by
-// (tile, sequence) in groups of the Hkv heads' tiles: a paged pool takes the group's
-// place from the page table (the caller reads page_table[b][t]); a contiguous pool puts
-// group (t, b) at t*B + b, so tile t of every sequence lies side by side and the
-// streams that read all sequences' prefixes at once stay within one window of memory.
-__device__ __forceinline__ size_t tile_offset(bool paged, int page, int B, int Hkv, int d, int b, int g, int t) {
-  const size_t group = paged ? (size_t)page : (size_t)t * B + b;
-  return (group * Hkv + g) * 64 * d;
+// level's K or V^T pool (both hold 64*d elements per tile).  Paged pool: tile g of the
+// physical page `page` (the caller reads page_table[b][t]), pages being the Hkv heads'
+// tiles of one (sequence, 64 entries).  Contiguous pool of capacity cap (T = cap/64
+// tiles per (b, g)): the tiles come in runs of kTileRun consecutive tiles of one (b, g);
+// the runs covering tiles [R*q, R*q + R) of every (b, g) are side by side, in (b, g)
+// order, run range after run range; the last T mod R tiles of each (b, g) follow, (b, g)
+// after (b, g).  The workgroups streaming every sequence's prefix at once thus read
+// within one window of memory rather than at a fixed stride of one sequence's pool,
+// while each still reads runs of 256 KB (K) in order.
+__device__ __forceinline__ size_t tile_offset(bool paged, int page, int cap, int B, int Hkv, int d, int b, int g,
+                                              int t) {
+  size_t tile;
+  if (paged) {
+    tile = (size_t)page * Hkv + g;
+  } else {
+    const int T = cap / 64, full = T / kTileRun;  // complete run ranges
+    const int q = t / kTileRun, w = t - q * kTileRun;
+    tile = q < full ? (((size_t)q * B + b) * Hkv + g) * kTileRun + w
+                    : (size_t)full * B * Hkv * kTileRun + ((size_t)b * Hkv + g) * (T - full * kTileRun) + w;
+  }
+  return tile * 64 * d;
 }
 
 // Physical page of tile t of sequence b in a level (0 for a contiguous pool); false if the

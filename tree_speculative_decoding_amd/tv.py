@@ -25,6 +25,7 @@ TV_SEQ_OK, TV_SEQ_BAD_PARENT, TV_SEQ_POOL_FULL, TV_SEQ_BAD_PREFIX, TV_SEQ_BAD_PA
 TV_MAX_LEVELS = 2
 TV_MAX_D = 64
 TV_POOL_ALIGN = 64
+TV_TILE_RUN = 16
 
 
 class TvError(RuntimeError):
@@ -163,13 +164,28 @@ def round_cap(n: int) -> int:
     return max(TV_POOL_ALIGN, -(-n // TV_POOL_ALIGN) * TV_POOL_ALIGN)
 
 
+def contiguous_tile_index(B: int, Hkv: int, cap: int) -> np.ndarray:
+    """[B][Hkv][cap/64] int64: the tile of a contiguous pool that holds tile t of (sequence b,
+    KV head g) (runs of TV_TILE_RUN tiles of one (b, g), run ranges of all (b, g) side by
+    side, the last T mod R tiles of each (b, g) at the end; include/tv.h).  Layout only."""
+    R, T = TV_TILE_RUN, cap // TV_POOL_ALIGN
+    full = T // R
+    b = np.arange(B)[:, None, None]
+    g = np.arange(Hkv)[None, :, None]
+    t = np.arange(T)[None, None, :]
+    q, w = t // R, t % R
+    in_run = ((q * B + b) * Hkv + g) * R + w
+    tail = full * B * Hkv * R + (b * Hkv + g) * (T - full * R) + w
+    return np.where(q < full, in_run, tail).astype(np.int64)
+
+
 class DeviceState:
     """Device tensors of a tv_state: pools (K row-major, V transposed), counts, open
     sums, tail and committed lengths.  Allocation and data movement only; no arithmetic.
 
-    Contiguous pools are [cap/64][B][Hkv][64][d] (K) and [cap/64][B][Hkv][d][64] (V^T):
-    tile t of every sequence side by side; logical_k / logical_vt give the per-sequence
-    views.
+    Contiguous pools are B*Hkv*cap/64 tiles, [64][d] (K) and [d][64] (V^T), placed as
+    contiguous_tile_index says (runs of TV_TILE_RUN tiles per (sequence, head), the
+    sequences' runs side by side); logical_k / logical_vt give the per-sequence views.
 
     With ``page_seed`` set the pools are paged: each level holds B * cap/64 (+ ``spare_pages``)
     physical pages of 64 entries for all KV heads, and a page table maps every
@@ -198,10 +214,11 @@ class DeviceState:
                 self.num_pages.append(npg)
                 self.pool_k.append(z(npg, Hkv, A, d))
                 self.pool_vt.append(z(npg, Hkv, d, A))
-        else:  # tile t of every sequence side by side: [cap/64][B][Hkv][...]
+        else:  # tiles placed as contiguous_tile_index says
             self.page_table, self.num_pages = None, None
-            self.pool_k = [z(c // A, B, Hkv, A, d) for c in self.caps]
-            self.pool_vt = [z(c // A, B, Hkv, d, A) for c in self.caps]
+            self.pool_k = [z(B * Hkv * (c // A), A, d) for c in self.caps]
+            self.pool_vt = [z(B * Hkv * (c // A), d, A) for c in self.caps]
+            self.tile_index = [torch.from_numpy(contiguous_tile_index(B, Hkv, c)).to(device) for c in self.caps]
         self.n = [z(B, dt=torch.int32) for _ in self.levels]
         self.open_k = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
         self.open_v = [z(B, Hkv, d, dt=torch.float32) for _ in self.levels]
@@ -243,12 +260,13 @@ class DeviceState:
         A = TV_POOL_ALIGN
         n = k.shape[1]
         if not self.paged:  # K: only entries < n are written; V^T: whole tiles
+            idx = self.tile_index[l][b]  # [Hkv][cap/64]
             full, r = n // A, n % A
             if full:
-                self.pool_k[l][:full, b] = k[:, :full * A].reshape(self.Hkv, full, A, self.d).permute(1, 0, 2, 3)
+                self.pool_k[l][idx[:, :full].reshape(-1)] = k[:, :full * A].reshape(self.Hkv * full, A, self.d)
             if r:
-                self.pool_k[l][full, b, :, :r] = k[:, full * A:n]
-            self.pool_vt[l][:, b] = vt.permute(1, 0, 2, 3)
+                self.pool_k[l][idx[:, full], :r] = k[:, full * A:n]
+            self.pool_vt[l][idx.reshape(-1)] = vt.reshape(-1, self.d, A)
             return
         pps = self.caps[l] // A
         pages = self.page_table[l][b].long()
@@ -258,18 +276,18 @@ class DeviceState:
         self.pool_vt[l][pages] = vt.permute(1, 0, 2, 3)
 
     def logical_k(self, l: int) -> torch.Tensor:
-        """Level l's K pool as [B][Hkv][cap][d] (a copy)."""
+        """Level l's K pool as [B][Hkv][cap][d] (a gather)."""
         if not self.paged:
-            return self.pool_k[l].permute(1, 2, 0, 3, 4).reshape(self.B, self.Hkv, self.caps[l], self.d)
+            return self.pool_k[l][self.tile_index[l].reshape(-1)].reshape(self.B, self.Hkv, self.caps[l], self.d)
         A = TV_POOL_ALIGN
         g = self.pool_k[l][self.page_table[l].long()]  # [B][pps][Hkv][64][d]
         return g.permute(0, 2, 1, 3, 4).reshape(self.B, self.Hkv, self.caps[l], self.d)
 
     def logical_vt(self, l: int) -> torch.Tensor:
-        """Level l's V tiles as [B][Hkv][cap/64][d][64] (a view of a contiguous pool, a
-        gather of a paged one)."""
+        """Level l's V tiles as [B][Hkv][cap/64][d][64] (a gather)."""
         if not self.paged:
-            return self.pool_vt[l].permute(1, 2, 0, 3, 4)
+            T = self.caps[l] // TV_POOL_ALIGN
+            return self.pool_vt[l][self.tile_index[l].reshape(-1)].reshape(self.B, self.Hkv, T, self.d, TV_POOL_ALIGN)
         g = self.pool_vt[l][self.page_table[l].long()]  # [B][pps][Hkv][d][64]
         return g.permute(0, 2, 1, 3, 4)
 
