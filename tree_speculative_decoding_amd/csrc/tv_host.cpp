@@ -97,8 +97,8 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Prefix-stream partition (see AttnArgs).  Auto mode runs one round of persistent
 // workgroups, as many as fit on the device at once (two per CU for both kernels), but
-// keeps at least 16 chunks (1024 entries) per workgroup so that the partials stay a few
-// percent of the streamed bytes.
+// keeps at least 4 chunks (256 entries) per workgroup: small prefixes are latency-bound,
+// and spreading them wide pays for partials up to a quarter of the streamed bytes.
 Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   Plan p{};
   const int G = Hq / st->Hkv;
@@ -118,7 +118,7 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
       want = num_parts;
     } else {
       want = (long long)device_cus() * 2;
-      const long long by_size = (total + 15) / 16;
+      const long long by_size = (total + 3) / 4;
       if (want > by_size) want = by_size;
     }
     if (want > total) want = total;
