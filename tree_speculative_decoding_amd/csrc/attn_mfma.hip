@@ -32,6 +32,7 @@
 // workgroup's slice covers the whole unit it normalises and writes the output rows and
 // their LSE; otherwise every workgroup of the unit writes a partial (running max, sum,
 // unnormalised output) for the merge kernel.
+#include "scratch_pad.h"
 #include "tv_launch.h"
 
 namespace tv {
@@ -77,17 +78,23 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, grp = lane >> 4;
+  if ((int)blockIdx.x < a.fold_scratch) {  // a scratch-pad workgroup (uniform)
+    const int sb = blockIdx.x / a.D;
+    scratch_node<uint16_t, 4>(a, sb, blockIdx.x - sb * a.D, (int*)smem);  // (4: no spill beside the stream's registers)
+    return;
+  }
+  const int part = blockIdx.x - a.fold_scratch;  // this workgroup's slice of the stream
   uint4 kpa[PER], vpa[PER], kpb[PER], vpb[PER];  // two chunks of loads in flight
 
   // this workgroup's slice of the units' chunks, laid end to end
   const long long total = a.units * a.tmax;
-  long long cg = (long long)blockIdx.x * a.per;
+  long long cg = (long long)part * a.per;
   const long long cend = min(cg + a.per, total);
   while (cg < cend) {
     const long long u = cg / a.tmax;
     const int c_first = (int)(cg - u * a.tmax);
     const int c_last = (int)min((long long)a.tmax, cend - u * a.tmax);
-    const int slot = (int)(blockIdx.x - unit_first_part(u, a.tmax, a.per));
+    const int slot = (int)(part - unit_first_part(u, a.tmax, a.per));
     const bool whole_unit = c_first == 0 && c_last == a.tmax;  // no other workgroup touches it
     const int rb = (int)(u % a.row_blocks);
     const int g = (int)((u / a.row_blocks) % a.Hkv);
@@ -493,13 +500,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   const int tt = a.fused_tree ? a.tree_tiles : 1;
   const bool paged = a.pt[0] != nullptr;  // every level or none
   if (paged) {
-    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, true>), dim3(a.parts), dim3(256), 0, s, a);
-    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, true>), dim3(a.parts), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_mfma<4, 4, true>), dim3(a.parts), dim3(256), 0, s, a);
+    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, true>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
+    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, true>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_mfma<4, 4, true>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
   } else {
-    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, false>), dim3(a.parts), dim3(256), 0, s, a);
-    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, false>), dim3(a.parts), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_mfma<4, 4, false>), dim3(a.parts), dim3(256), 0, s, a);
+    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, false>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
+    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, false>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_mfma<4, 4, false>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -1,133 +1,16 @@
-// Chain-wise compression of every tree node's own branch into the scratch pad.
-// TSD-V4 §4.1 (chains share the prefix state but are compressed independently after
-// branching; one compression never mixes two chains) and §4.2 (per-chain compressed
-// tokens and intermediate sums stay in the scratch pad until the path is accepted).
-//
-// Node i sits at position pos = P + depth(i); its block of a level with size C starts at
-// b0 = floor(pos/C)*C.  The block sum is the committed open sum (only if b0 < P, i.e. the
-// block began before the tree) plus the chain's tokens at positions >= b0, added in chain
-// order (root first) in fp32.  A node whose position ends a block writes the entry sum/C
-// (rounded once to the element type) and a zero open sum; any other node writes the
-// running sum.
-//
-// The pad depends on the tree tokens, the plan and the committed open sums only, not on
-// the prefix, so it is built by its own short kernel ahead of the prefix stream.  One
-// workgroup per (sequence, node) with the tree's depths in LDS; thread t takes the four
-// consecutive elements 4t .. 4t+3 of the node's Hkv*d row (per pass of 1024) and walks
-// the node's chain once for every level, issuing the K and V loads of up to eight chain
-// nodes before adding them in chain order.
+// The scratch pad kernel: one workgroup per (sequence, node) (scratch_node, in
+// scratch_pad.h), launched ahead of the prefix stream unless the prefix kernel builds the
+// pad in workgroups of its own launch.  TSD-V4 §4.1, §4.2.
+#include "scratch_pad.h"
 #include "tv_launch.h"
 
 namespace tv {
 
-// Four consecutive elements: loads and stores of 8 (bf16) or 16 (fp32) bytes.
-template <typename T> struct Quad;
-template <> struct Quad<float> {
-  static __device__ __forceinline__ float4 load(const float* p, size_t i) { return *(const float4*)(p + i); }
-  static __device__ __forceinline__ void store(float* p, size_t i, float4 v) { *(float4*)(p + i) = v; }
-};
-template <> struct Quad<uint16_t> {
-  static __device__ __forceinline__ float4 load(const uint16_t* p, size_t i) {
-    const uint2 r = *(const uint2*)(p + i);
-    return make_float4(bf16_bits_to_f32(r.x & 0xffffu), bf16_bits_to_f32(r.x >> 16),
-                       bf16_bits_to_f32(r.y & 0xffffu), bf16_bits_to_f32(r.y >> 16));
-  }
-  static __device__ __forceinline__ void store(uint16_t* p, size_t i, float4 v) {
-    *(uint2*)(p + i) = make_uint2((uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
-                                  (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
-  }
-};
-
-__device__ __forceinline__ float4 add4(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void k_scratch(AttnArgs a) {
-  constexpr int kBatch = 8;  // chain nodes whose loads are issued together
   __shared__ int dep_s[TV_MAX_D];
   const int b = blockIdx.x / a.D;
-  const int i = blockIdx.x - b * a.D;
-  const int tid = threadIdx.x;
-  // every load that needs no other load's result goes out in one round trip (issued by
-  // every lane, without branches): the depths, the status, P, the node's chain
-  const int dval = a.depth[(size_t)b * a.anc_ld + (tid < a.D ? tid : 0)];
-  const int eval = *(a.seq_err != nullptr ? a.seq_err + b : a.P + b);
-  const int P = a.P[b];
-  const uint64_t chain = a.anc[(size_t)b * a.anc_ld + i] & node_mask(a.D);
-  // (an empty use of all four: the compiler issues them together and waits once, instead
-  // of moving each load down to its first use)
-  asm volatile("" ::"v"(dval), "v"(eval), "v"(P), "v"((uint32_t)chain), "v"((uint32_t)(chain >> 32)));
-  if (tid < a.D) dep_s[tid] = dval;
-  __syncthreads();
-  if (a.seq_err != nullptr && eval != TV_SEQ_OK) return;  // uniform
-
-  const int pos = P + dep_s[i];
-  int b0[TV_MAX_LEVELS];
-#pragma unroll
-  for (int l = 0; l < TV_MAX_LEVELS; ++l) b0[l] = l < a.n_levels ? (pos / a.C[l]) * a.C[l] : 0;
-  const int HD = a.Hkv * a.d;  // a multiple of 64
-  const T* kt = (const T*)a.k_tree;
-  const T* vt = (const T*)a.v_tree;
-  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-
-  for (int e = 4 * tid; e < HD; e += 4 * 256) {
-    float4 sk[TV_MAX_LEVELS], sv[TV_MAX_LEVELS];
-#pragma unroll
-    for (int l = 0; l < TV_MAX_LEVELS; ++l) {
-      const bool use_open = l < a.n_levels && b0[l] < P;
-      const size_t so = (size_t)b * HD + e;
-      sk[l] = use_open ? *(const float4*)(a.open_k[l] + so) : z;
-      sv[l] = use_open ? *(const float4*)(a.open_v[l] + so) : z;
-    }
-    // the chain, root first, kBatch nodes at a time: every load of a batch, then the
-    // additions in chain order
-    uint64_t mm = chain;
-    while (mm != 0ull) {
-      int js[kBatch];
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t) {
-        js[t] = mm != 0ull ? __builtin_ctzll(mm) : -1;
-        if (mm != 0ull) mm &= mm - 1ull;
-      }
-      float4 kk[kBatch], vv[kBatch];
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t) {
-        const size_t o = ((size_t)b * a.D + (js[t] >= 0 ? js[t] : 0)) * HD + e;
-        kk[t] = js[t] >= 0 ? Quad<T>::load(kt, o) : z;
-        vv[t] = js[t] >= 0 ? Quad<T>::load(vt, o) : z;
-      }
-#pragma unroll
-      for (int t = 0; t < kBatch; ++t) {
-        if (js[t] < 0) break;
-        const int pj = P + dep_s[js[t]];
-#pragma unroll
-        for (int l = 0; l < TV_MAX_LEVELS; ++l)
-          if (l < a.n_levels && pj >= b0[l]) {
-            sk[l] = add4(sk[l], kk[t]);
-            sv[l] = add4(sv[l], vv[t]);
-          }
-      }
-    }
-#pragma unroll
-    for (int l = 0; l < TV_MAX_LEVELS; ++l) {
-      if (l >= a.n_levels) break;
-      const int C = a.C[l];
-      const size_t dst = ((size_t)b * a.D + i) * HD + e;
-      if ((pos + 1) % C == 0) {
-        const float cf = (float)C;
-        Quad<T>::store((T*)a.scratch.entry_k[l], dst,
-                       make_float4(sk[l].x / cf, sk[l].y / cf, sk[l].z / cf, sk[l].w / cf));
-        Quad<T>::store((T*)a.scratch.entry_v[l], dst,
-                       make_float4(sv[l].x / cf, sv[l].y / cf, sv[l].z / cf, sv[l].w / cf));
-        *(float4*)(a.scratch.open_k[l] + dst) = z;
-        *(float4*)(a.scratch.open_v[l] + dst) = z;
-      } else {
-        *(float4*)(a.scratch.open_k[l] + dst) = sk[l];
-        *(float4*)(a.scratch.open_v[l] + dst) = sv[l];
-      }
-    }
-  }
+  scratch_node<T>(a, b, blockIdx.x - b * a.D, dep_s);
 }
 
 hipError_t launch_scratch(const AttnArgs& a, hipStream_t s) {

@@ -145,6 +145,9 @@ struct AttnArgs {
   int fused_tree;                    // the MFMA prefix kernel also attends to the raw tail and
                                      // the tree chunk, and writes whole units' rows itself
   int tree_tiles;                    // 16-entry tiles of that chunk: 1, 2 or 4
+  int fold_scratch;                  // MFMA prefix kernel: its first fold_scratch workgroups
+                                     // build the scratch pad (one per (sequence, node)), the
+                                     // prefix stream's `parts` workgroups follow
   float* ws_o;                       // [B][Hkv][smax][R][d]
   float2* ws_ml;                     // [B][Hkv][smax][R] (running max in log2 units, sum)
   float scale_log2;                  // log2(e) / sqrt(d)

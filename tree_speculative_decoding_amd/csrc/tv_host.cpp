@@ -91,6 +91,7 @@ struct Plan {
   int R, row_blocks, tmax, parts, smax;
   long long units, per;
   size_t ws_o_bytes, ws_ml_off, total;
+  bool fold;  // the MFMA prefix launch has room for the scratch pad's B*D workgroups
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -114,12 +115,23 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
     p.smax = 0;
   } else {
     long long want;
+    const long long slots = (long long)device_cus() * 2;  // workgroups resident at once
+    const long long pad = (long long)st->B * D;             // scratch-pad workgroups
     if (num_parts > 0) {
       want = num_parts;
+      p.fold = want + pad <= slots;
     } else {
-      want = (long long)device_cus() * 2;
+      want = slots;
       const long long by_size = (total + 3) / 4;
       if (want > by_size) want = by_size;
+      // the scratch pad rides in the same launch when the stream leaves room for it, or
+      // when it is a handful of workgroups (taken from the stream's)
+      if (want + pad <= slots) {
+        p.fold = true;
+      } else if (pad <= 16 && pad < want) {
+        want = slots - pad;
+        p.fold = true;
+      }
     }
     if (want > total) want = total;
     if (want < 1) want = 1;
@@ -196,9 +208,13 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
   const int tree_entries = D + (c0 - 1);
   a.fused_tree = mfma && p.parts > 0 && tree_entries <= 64;
   a.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
-  // the scratch pad needs only the tree tokens, the plan and the committed open sums
-  s = hip_check(tv::launch_scratch(a, stream), "scratch pad launch");
-  if (s != TV_OK) return s;
+  // the scratch pad needs only the tree tokens, the plan and the committed open sums: in
+  // workgroups of the MFMA prefix launch when it has room, else a short kernel ahead of it
+  a.fold_scratch = (mfma && p.fold && p.parts > 0 && a.build_scratch && st->n_levels > 0) ? st->B * D : 0;
+  if (a.fold_scratch == 0) {
+    s = hip_check(tv::launch_scratch(a, stream), "scratch pad launch");
+    if (s != TV_OK) return s;
+  }
   if (g_ev_start) {
     s = hip_check(hipEventRecord(g_ev_start, stream), "timing event");
     if (s != TV_OK) return s;
