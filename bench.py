@@ -526,20 +526,22 @@ def main():
 
 def read_ceiling(stream, gib: int = 4) -> dict:
     """The device's practical HBM read ceiling: a plain read-reduce kernel (libtv_measure.so)
-    over `gib` GiB, launched with 2, 4 and 8 workgroups per CU, 5 timed launches each
-    (fence-free events on `stream`); the best average."""
+    over `gib` GiB, with plain and with nontemporal loads, launched with 2, 4 and 8
+    workgroups per CU, 5 timed launches each (fence-free events on `stream`); the best
+    average."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "tree_speculative_decoding_amd", "libtv_measure.so"))
     lib.tvm_read_stream.restype = ctypes.c_int
-    lib.tvm_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tvm_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p]
     nbytes = gib << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.zeros(cus * 8, dtype=torch.int32, device="cuda")
     best, rows = 0.0, {}
-    for per_cu in (2, 4, 8):
-        launch = lambda: lib.tvm_read_stream(buf.data_ptr(), nbytes, cus * per_cu, sink.data_ptr(),
+    for nt, per_cu in [(nt, n) for nt in (0, 1) for n in (2, 4, 8)]:
+        launch = lambda: lib.tvm_read_stream(buf.data_ptr(), nbytes, cus * per_cu, nt, sink.data_ptr(),
                                              stream.cuda_stream)
         if launch() != 0:
             raise RuntimeError("tvm_read_stream failed")
@@ -550,12 +552,12 @@ def read_ceiling(stream, gib: int = 4) -> dict:
             record(b_, stream)
         torch.cuda.synchronize()
         gbs = nbytes / (float(np.mean([a_.elapsed_ms(b_) for a_, b_ in ev])) * 1e-3) / 1e9
-        rows[f"{per_cu}_per_cu"] = round(gbs, 1)
+        rows[f"{per_cu}_per_cu{'_nt' if nt else ''}"] = round(gbs, 1)
         best = max(best, gbs)
     del buf
     torch.cuda.empty_cache()
     return {"GB/s": round(best, 1), "frac_of_peak": round(best / PEAK_HBM_GBS, 4), "bytes": nbytes,
-            "by_workgroups": rows, "kernel": "plain read-reduce, 16-byte loads, 8 in flight per thread"}
+            "by_workgroups": rows, "kernel": "plain read-reduce, 16-byte loads (plain or nontemporal), 8 in flight per thread"}
 
 
 SWEEP_P = 131072

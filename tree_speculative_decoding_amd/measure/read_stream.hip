@@ -6,6 +6,8 @@
 //
 // Grid-stride loop, 16-byte loads, 8 loads in flight per thread before any use; each
 // workgroup XORs what it read into one word (so no load can be dropped) and writes it.
+// The loads are plain or carry the nontemporal hint (the verify kernel streams its pools
+// with the hint; on MI355X the hinted read is the faster one).
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -14,8 +16,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kInFlight = 8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kThreads) void k_read_stream(const uint4* __restrict__ p, size_t n16,
+template <bool kNT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if (kNT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool kNT>
+__global__ __launch_bounds__(kThreads) void k_read_stream(const u32x4* __restrict__ p, size_t n16,
                                                           uint32_t* __restrict__ sink) {
   __shared__ uint32_t red[kThreads / 64];
   uint32_t acc = 0;
@@ -23,15 +33,15 @@ __global__ __launch_bounds__(kThreads) void k_read_stream(const uint4* __restric
   const size_t stride = (size_t)gridDim.x * span;
   size_t i = (size_t)blockIdx.x * span + threadIdx.x;
   for (; i + (kInFlight - 1) * kThreads < n16; i += stride) {
-    uint4 v[kInFlight];
+    u32x4 v[kInFlight];
 #pragma unroll
-    for (int x = 0; x < kInFlight; ++x) v[x] = p[i + (size_t)x * kThreads];
+    for (int x = 0; x < kInFlight; ++x) v[x] = load16<kNT>(p + i + (size_t)x * kThreads);
 #pragma unroll
     for (int x = 0; x < kInFlight; ++x) acc ^= v[x].x ^ v[x].y ^ v[x].z ^ v[x].w;
   }
   // the ragged end of the buffer (fewer than kInFlight * kThreads chunks in this stride)
   for (; i < n16; i += kThreads) {
-    const uint4 v = p[i];
+    const u32x4 v = load16<kNT>(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
@@ -47,12 +57,17 @@ __global__ __launch_bounds__(kThreads) void k_read_stream(const uint4* __restric
 }  // namespace
 
 // Reads `bytes` (a multiple of 16) from device buffer `p` with `blocks` workgroups of 256
-// threads on `stream`; workgroup w writes the XOR of the words it read to sink[w] (a
-// device buffer of at least `blocks` words).  Returns 0 on success, else the HIP error
-// code (-1 for a bad argument; nothing is launched then).
+// threads on `stream`, with nontemporal loads when `nontemporal` is nonzero; workgroup w
+// writes the XOR of the words it read to sink[w] (a device buffer of at least `blocks`
+// words).  Returns 0 on success, else the HIP error code (-1 for a bad argument; nothing
+// is launched then).
 extern "C" __attribute__((visibility("default"))) int tvm_read_stream(const void* p, size_t bytes, int blocks,
-                                                                      uint32_t* sink, hipStream_t stream) {
+                                                                      int nontemporal, uint32_t* sink,
+                                                                      hipStream_t stream) {
   if (p == nullptr || sink == nullptr || blocks < 1 || bytes % 16 != 0 || ((uintptr_t)p & 15) != 0) return -1;
-  hipLaunchKernelGGL(k_read_stream, dim3(blocks), dim3(kThreads), 0, stream, (const uint4*)p, bytes / 16, sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(k_read_stream<true>, dim3(blocks), dim3(kThreads), 0, stream, (const u32x4*)p, bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(k_read_stream<false>, dim3(blocks), dim3(kThreads), 0, stream, (const u32x4*)p, bytes / 16, sink);
   return (int)hipGetLastError();
 }
