@@ -25,6 +25,8 @@ MULTI = {
     "f32_c4_c16": (synth.Workload("ms2", 4, 7, 8, 2, 64, "f32", (4, 16), 13, 2, 3, 0.6, 3002, prefix="raw"), 40),
     "bf16_linear": (synth.Workload("ms3", 2, 8, 16, 2, 128, "bf16", (4, 128), 250, 1, 7, 0.9, 3003, prefix="raw"), 30),
     "bf16_c1_c4": (synth.Workload("ms4", 2, 6, 8, 1, 128, "bf16", (1, 4), 9, 2, 3, 0.7, 3004, prefix="raw"), 25),
+    # a raw tail of up to 7 tokens: the new tail tokens of one step take more than one batch
+    "bf16_c8_c32": (synth.Workload("ms5", 2, 8, 16, 2, 128, "bf16", (8, 32), 250, 1, 7, 0.9, 3005, prefix="raw"), 30),
 }
 
 
@@ -143,6 +145,7 @@ FUSED = {
     "bf16_c4_c128": (synth.Workload("fu1", 4, 8, 16, 2, 128, "bf16", (4, 128), 122, 2, 3, 0.8, 3301, prefix="raw"), 40),
     "f32_d64_c4_c16": (synth.Workload("fu2", 3, 7, 8, 2, 64, "f32", (4, 16), 13, 2, 3, 0.6, 3302, prefix="raw"), 30),
     "bf16_chain_c1_c4": (synth.Workload("fu3", 2, 8, 8, 1, 128, "bf16", (1, 4), 9, 1, 7, 0.9, 3303, prefix="raw"), 25),
+    "bf16_chain_c8_c32": (synth.Workload("fu4", 2, 8, 16, 2, 128, "bf16", (8, 32), 250, 1, 7, 0.9, 3304, prefix="raw"), 25),
 }
 
 

@@ -17,87 +17,174 @@
 
 namespace tv {
 
-// The refresh of sequence b once its accepted path is in LDS (pth[0..m], m < D checked
-// by the caller's path validation into path_bad) and every thread has read the old
-// counters: P is sequence b's committed length before the refresh.
+// LDS of a refresh workgroup: the accepted path, the blocks it commits and the
+// validation flags (bit 0: a path node out of range, bit 1: a page missing).
+struct RefreshLds {
+  static constexpr int kMaxCommits = 2 * (TV_MAX_D + 1);  // per level at most (m + 1)/C + 1
+  int pth[TV_MAX_D];
+  int it_l[kMaxCommits], it_j[kMaxCommits], it_u[kMaxCommits], it_page[kMaxCommits];
+  int bad;
+};
+
+// A storage element's bits, widened to 32 (so that no two elements share a register).
+template <typename T>
+struct Bits;
+template <>
+struct Bits<uint16_t> {
+  static __device__ __forceinline__ uint32_t ld(const uint16_t* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(uint16_t* p, size_t i, uint32_t v) { p[i] = (uint16_t)v; }
+};
+template <>
+struct Bits<float> {
+  static __device__ __forceinline__ uint32_t ld(const float* p, size_t i) { return __float_as_uint(p[i]); }
+  static __device__ __forceinline__ void st(float* p, size_t i, uint32_t v) { p[i] = __uint_as_float(v); }
+};
+
+// Commits and tail tokens whose loads are issued together, ahead of any store (the
+// common trees need one batch of each; longer accepted paths take more).
+constexpr int kCommitBatch = 8;
+constexpr int kTailBatch = 4;
+
+// The refresh of sequence b: sh.pth[0..m] holds the accepted path and sh.bad is 0 (both
+// behind a barrier), and every thread has read the old counters: P is the sequence's
+// committed length before the refresh.  The threads first list the blocks the path
+// closes (one thread per block: its level, slot, closing node and page), checking the
+// path and the pages; then each thread copies its channels of every listed entry, the
+// leaf's open sums and the new tail tokens, with all of a batch's loads issued before its
+// stores (the sources, scratch pad and tree tokens, are never written here).
 template <typename T>
 __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, const tv_scratch& sc,
                                              const T* __restrict__ k_tree, const T* __restrict__ v_tree, int m,
-                                             int P, const int* pth, bool path_bad, int32_t* __restrict__ commit_log,
+                                             int P, RefreshLds& sh, int32_t* __restrict__ commit_log,
                                              int32_t* __restrict__ seq_err) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int L = st.n_levels;
   const int Hkv = st.Hkv, d = st.d, HD = Hkv * d;
-  if (m >= D || P < 0 || path_bad) {
+  if (m >= D || P < 0) {  // uniform
     if (tid == 0) seq_err[b] = TV_SEQ_BAD_PATH;
     return;
   }
   const int P2 = P + m + 1;
   bool full = false;
-  for (int l = 0; l < L; ++l) full |= (P2 / st.lvl[l].C) > st.lvl[l].cap;
-  if (full) {
-    if (tid == 0) seq_err[b] = TV_SEQ_POOL_FULL;
-    return;
-  }
-  // every page the commits write must exist (paged pools), else nothing changes
-  bool page_bad = false;
-  for (int l = 0; l < L; ++l)
-    for (int j = P / st.lvl[l].C; j < P2 / st.lvl[l].C; ++j) {
-      int page;
-      page_bad |= !tile_page(st.lvl[l], b, j >> 6, &page);
-    }
-  if (page_bad) {
-    if (tid == 0) seq_err[b] = TV_SEQ_BAD_PAGE;
-    return;
-  }
-  const int leaf = pth[m];
+  int j0[2] = {0, 0}, nc[2] = {0, 0};
   for (int l = 0; l < L; ++l) {
-    const int C = st.lvl[l].C;
-    T* pk = (T*)st.lvl[l].k;
-    T* pvt = (T*)st.lvl[l].vt;
-    const T* ek = (const T*)sc.entry_k[l];
-    const T* ev = (const T*)sc.entry_v[l];
-    const int j0 = P / C, j1 = P2 / C;
-    for (int j = j0; j < j1; ++j) {
-      const int u = pth[j * C + C - 1 - P];  // path node at the block's last position
-      int page;
-      tile_page(st.lvl[l], b, j >> 6, &page);  // checked above
-      for (int e = tid; e < HD; e += nt) {
-        const int g = e / d, dd = e - g * d;
-        const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
-        const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, st.lvl[l].cap, st.B, Hkv, d, b, g, j >> 6);
-        pk[tb + (size_t)(j & 63) * d + dd] = ek[src];
-        pvt[tb + (size_t)dd * 64 + (j & 63)] = ev[src];
-      }
-      if (commit_log != nullptr && tid == 0) {
-        int32_t* row = commit_log + (((size_t)b * L + l) * D + (j - j0)) * 2;
-        row[0] = j;
-        row[1] = u;
-      }
-    }
-    const float* sok = sc.open_k[l] + ((size_t)b * D + leaf) * HD;
-    const float* sov = sc.open_v[l] + ((size_t)b * D + leaf) * HD;
-    for (int e = tid; e < HD; e += nt) {
-      st.lvl[l].open_k[(size_t)b * HD + e] = sok[e];
-      st.lvl[l].open_v[(size_t)b * HD + e] = sov[e];
-    }
+    full |= (P2 / st.lvl[l].C) > st.lvl[l].cap;
+    j0[l] = P / st.lvl[l].C;
+    nc[l] = P2 / st.lvl[l].C - j0[l];
   }
-  if (L > 0 && st.lvl[0].C > 1) {
-    const int C0 = st.lvl[0].C;
-    const int t_new = (P2 / C0) * C0;
-    T* tk = (T*)st.tail_k;
-    T* tv_ = (T*)st.tail_v;
-    // positions below P keep their slot when no block closed (t_new == old start);
-    // when one closed, t_new > P and only path tokens remain
-    for (int pos = max(t_new, P); pos < P2; ++pos) {
-      const int u = pth[pos - P];
-      for (int e = tid; e < HD; e += nt) {
-        const int g = e / d, dd = e - g * d;
-        const size_t src = (((size_t)b * D + u) * Hkv + g) * d + dd;
-        const size_t dst = (((size_t)b * Hkv + g) * (C0 - 1) + (pos - t_new)) * d + dd;
-        tk[dst] = k_tree[src];
-        tv_[dst] = v_tree[src];
+  const int ncom = nc[0] + nc[1];
+  if (tid <= m && (sh.pth[tid] < 0 || sh.pth[tid] >= D)) atomicOr(&sh.bad, 1);
+  if (!full && tid < ncom) {
+    const bool l1 = tid >= nc[0];  // levels are picked by selection, not by a run-time index
+    const tv_level& lv = l1 ? st.lvl[1] : st.lvl[0];
+    const int C = lv.C;
+    const int j = l1 ? j0[1] + tid - nc[0] : j0[0] + tid;
+    int page;
+    if (!tile_page(lv, b, j >> 6, &page)) atomicOr(&sh.bad, 2);
+    sh.it_l[tid] = l1 ? 1 : 0;
+    sh.it_j[tid] = j;
+    sh.it_u[tid] = sh.pth[j * C + C - 1 - P];  // path node at the block's last position
+    sh.it_page[tid] = page;
+  }
+  __syncthreads();
+  const int bad = sh.bad;
+  if (bad != 0 || full) {  // uniform; the state is left unchanged
+    if (tid == 0) seq_err[b] = (bad & 1) ? TV_SEQ_BAD_PATH : full ? TV_SEQ_POOL_FULL : TV_SEQ_BAD_PAGE;
+    return;
+  }
+  if (commit_log != nullptr && tid < ncom) {
+    const int l = sh.it_l[tid];
+    int32_t* row = commit_log + (((size_t)b * L + l) * D + (sh.it_j[tid] - (l ? j0[1] : j0[0]))) * 2;
+    row[0] = sh.it_j[tid];
+    row[1] = sh.it_u[tid];
+  }
+  const int leaf = sh.pth[m];
+  // the finest level's raw tail: positions [t0, P2) come from the path; positions below
+  // P keep their slot when no block closed (t_new == old start), when one closed t_new > P
+  // and only path tokens remain
+  const int C0 = L > 0 ? st.lvl[0].C : 1;
+  const int t_new = C0 > 1 ? (P2 / C0) * C0 : P2;
+  const int t0 = max(t_new, P);
+  const int ntail = C0 > 1 ? P2 - t0 : 0;
+  const T* ek0 = (const T*)sc.entry_k[0];
+  const T* ek1 = (const T*)sc.entry_k[1];
+  const T* ev0 = (const T*)sc.entry_v[0];
+  const T* ev1 = (const T*)sc.entry_v[1];
+  T* tail_k = (T*)st.tail_k;
+  T* tail_v = (T*)st.tail_v;
+  for (int e = tid; e < HD; e += nt) {
+    const int g = e / d, dd = e - g * d;
+    const size_t seq_rows = (size_t)b * D;
+    // loads: the leaf's open sums, the first tail tokens, the first commits.  Each value
+    // is held in a 32-bit register of its own and every load is unconditional behind a
+    // uniform test (a missing item re-reads item 0), so no load waits for another; the
+    // empty asm makes every load issue before the first store.
+    float osk0 = 0.f, osv0 = 0.f, osk1 = 0.f, osv1 = 0.f;
+    if (L > 0) {
+      osk0 = sc.open_k[0][(seq_rows + leaf) * HD + e];
+      osv0 = sc.open_v[0][(seq_rows + leaf) * HD + e];
+    }
+    if (L > 1) {
+      osk1 = sc.open_k[1][(seq_rows + leaf) * HD + e];
+      osv1 = sc.open_v[1][(seq_rows + leaf) * HD + e];
+    }
+    uint32_t tk[kTailBatch], tvv[kTailBatch];
+    if (ntail > 0) {
+#pragma unroll
+      for (int t = 0; t < kTailBatch; ++t) {
+        const size_t src = (seq_rows + sh.pth[t0 + (t < ntail ? t : 0) - P]) * HD + e;
+        tk[t] = Bits<T>::ld(k_tree, src);
+        tvv[t] = Bits<T>::ld(v_tree, src);
       }
+    }
+    uint32_t ck[kCommitBatch], cv[kCommitBatch];
+    for (int c0 = 0; c0 < ncom; c0 += kCommitBatch) {
+#pragma unroll
+      for (int t = 0; t < kCommitBatch; ++t) {
+        const int i = c0 + t < ncom ? c0 + t : c0;
+        const bool l1 = sh.it_l[i] != 0;
+        const size_t src = (seq_rows + sh.it_u[i]) * HD + e;
+        ck[t] = Bits<T>::ld(l1 ? ek1 : ek0, src);
+        cv[t] = Bits<T>::ld(l1 ? ev1 : ev0, src);
+      }
+      asm volatile("" ::"v"(ck[0]), "v"(ck[1]), "v"(ck[2]), "v"(ck[3]), "v"(ck[4]), "v"(ck[5]), "v"(ck[6]),
+                   "v"(ck[7]), "v"(cv[0]), "v"(cv[1]), "v"(cv[2]), "v"(cv[3]), "v"(cv[4]), "v"(cv[5]), "v"(cv[6]),
+                   "v"(cv[7]));
+#pragma unroll
+      for (int t = 0; t < kCommitBatch; ++t)
+        if (c0 + t < ncom) {  // uniform
+          const int i = c0 + t, j = sh.it_j[i];
+          const tv_level& lv = sh.it_l[i] != 0 ? st.lvl[1] : st.lvl[0];
+          const size_t tb = tile_offset(lv.page_table != nullptr, sh.it_page[i], lv.cap, st.B, Hkv, d, b, g, j >> 6);
+          Bits<T>::st((T*)lv.k, tb + (size_t)(j & 63) * d + dd, ck[t]);
+          Bits<T>::st((T*)lv.vt, tb + (size_t)dd * 64 + (j & 63), cv[t]);
+        }
+    }
+    if (L > 0) {
+      st.lvl[0].open_k[(size_t)b * HD + e] = osk0;
+      st.lvl[0].open_v[(size_t)b * HD + e] = osv0;
+    }
+    if (L > 1) {
+      st.lvl[1].open_k[(size_t)b * HD + e] = osk1;
+      st.lvl[1].open_v[(size_t)b * HD + e] = osv1;
+    }
+    const size_t tail_row = ((size_t)b * Hkv + g) * (C0 - 1);
+    for (int tb0 = 0; tb0 < ntail; tb0 += kTailBatch) {
+      if (tb0 > 0) {  // tail tokens past the first batch (C0 > kTailBatch + 1)
+#pragma unroll
+        for (int t = 0; t < kTailBatch; ++t) {
+          const size_t src = (seq_rows + sh.pth[t0 + (tb0 + t < ntail ? tb0 + t : tb0) - P]) * HD + e;
+          tk[t] = Bits<T>::ld(k_tree, src);
+          tvv[t] = Bits<T>::ld(v_tree, src);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kTailBatch; ++t)
+        if (tb0 + t < ntail) {  // uniform
+          const size_t dst = (tail_row + (t0 + tb0 + t - t_new)) * d + dd;
+          Bits<T>::st(tail_k, dst, tk[t]);
+          Bits<T>::st(tail_v, dst, tvv[t]);
+        }
     }
   }
   __syncthreads();
@@ -115,26 +202,22 @@ __global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch
                                                   const int32_t* __restrict__ path,
                                                   int32_t* __restrict__ commit_log,
                                                   int32_t* __restrict__ seq_err) {
-  __shared__ int pth[TV_MAX_D];
-  __shared__ int path_bad;
+  __shared__ RefreshLds sh;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int L = st.n_levels;
-  if (commit_log != nullptr)
-    for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
+  // every read of the inputs and the old counters in one round trip
   const int err = seq_err[b];
   const int m = m_in[b];
   const int P = st.P[b];
-  if (tid == 0) path_bad = 0;
+  const int pv = tid < D ? path[(size_t)b * D + tid] : -1;
+  if (commit_log != nullptr)
+    for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
+  if (tid < D) sh.pth[tid] = pv;
+  if (tid == 0) sh.bad = 0;
   __syncthreads();  // log prefill and the reads above happen before any later write
   if (err != TV_SEQ_OK || m < 0) return;
-  if (tid < D) {
-    const int v = path[(size_t)b * D + tid];
-    pth[tid] = v;
-    if (tid <= m && (v < 0 || v >= D)) atomicOr(&path_bad, 1);
-  }
-  __syncthreads();
-  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, pth, path_bad != 0, commit_log, seq_err);
+  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, sh, commit_log, seq_err);
 }
 
 // Acceptance and refresh in one launch (one workgroup per sequence): the first wave
@@ -154,9 +237,8 @@ __global__ __launch_bounds__(1024) void k_accept_refresh(int D, tv_state st, tv_
                                                          int32_t* __restrict__ bonus,
                                                          int32_t* __restrict__ commit_log,
                                                          int32_t* __restrict__ seq_err) {
-  __shared__ int pth[TV_MAX_D];
+  __shared__ RefreshLds sh;
   __shared__ int m_s;
-  __shared__ int path_bad;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int L = st.n_levels;
@@ -165,21 +247,19 @@ __global__ __launch_bounds__(1024) void k_accept_refresh(int D, tv_state st, tv_
   const int err = seq_err[b];
   const int P = st.P[b];
   if (tid < 64) {  // the first wave: every path slot -1, then the accepted path
-    if (tid < D) pth[tid] = -1;
-    const int m = accept_one(b, D, parents, anc, depth, draft, target, err, m_out, path, bonus, pth);
+    if (tid < D) sh.pth[tid] = -1;
+    const int m = accept_one(b, D, parents, anc, depth, draft, target, err, m_out, path, bonus, sh.pth);
     if (tid == 0) {
       m_s = m;
-      path_bad = 0;
+      sh.bad = 0;
     }
   }
   __syncthreads();  // the path is in LDS; the log prefill and the reads above are done
   const int m = m_s;
   if (err != TV_SEQ_OK || m < 0) return;
-  // slots 0..m hold one node each for a plan from tv_build_tree_mask; checked as
-  // tv_refresh_state checks a path it is given
-  if (tid < D && tid <= m && (pth[tid] < 0 || pth[tid] >= D)) atomicOr(&path_bad, 1);
-  __syncthreads();
-  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, pth, path_bad != 0, commit_log, seq_err);
+  // slots 0..m hold one node each for a plan from tv_build_tree_mask; refresh_body
+  // checks them as it checks a path it is given
+  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, sh, commit_log, seq_err);
 }
 
 hipError_t launch_accept_refresh(int D, const tv_state& st, const tv_scratch& sc, const int32_t* parents,
