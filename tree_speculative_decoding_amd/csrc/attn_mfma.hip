@@ -42,7 +42,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 constexpr int kDH = 128;        // head dim handled by this kernel
-constexpr int kXcds = 8;        // XCDs of an MI355X; workgroups go to them round-robin
 constexpr int kChunk = 64;      // entries per chunk
 constexpr int kKStr = kDH * 2 + 16;      // LDS bytes per K row (padded)
 constexpr int kVStr = kChunk * 2 + 16;   // LDS bytes per V^T row (padded)
@@ -93,17 +92,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     scratch_node<uint16_t, 4>(a, sb, blockIdx.x - sb * a.D, (int*)smem);  // (4: no spill beside the stream's registers)
     return;
   }
-  // This workgroup's slice of the stream.  Workgroup i runs on XCD i mod 8, and with one
-  // (sequence, KV head) prefix per slice the pool runs of slice p all have address bits
-  // 18-20 equal to its KV head p mod 8 (runs are 256 KB, heads innermost), so XCD x would
-  // read one eighth of the address space only; rotating the slices within each group of
-  // 8 workgroups gives every XCD every head (measured: the launch 1% shorter, and the
-  // XCDs' median stream times closer together).
-  int part = blockIdx.x - a.fold_scratch;
-  {
-    const int grp = part / kXcds, base = grp * kXcds;
-    if (base + kXcds <= a.parts) part = base + (part - base + grp) % kXcds;
-  }
+  const int part = blockIdx.x - a.fold_scratch;  // this workgroup's slice of the stream
   uint4 kpa[PER], vpa[PER], kpb[PER], vpb[PER];  // two chunks of loads in flight
 
   // this workgroup's slice of the units' chunks, laid end to end
