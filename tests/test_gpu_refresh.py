@@ -27,6 +27,9 @@ MULTI = {
     "bf16_c1_c4": (synth.Workload("ms4", 2, 6, 8, 1, 128, "bf16", (1, 4), 9, 2, 3, 0.7, 3004, prefix="raw"), 25),
     # a raw tail of up to 7 tokens: the new tail tokens of one step take more than one batch
     "bf16_c8_c32": (synth.Workload("ms5", 2, 8, 16, 2, 128, "bf16", (8, 32), 250, 1, 7, 0.9, 3005, prefix="raw"), 30),
+    # a 64-node chain accepted whole at C = 1 and 2: 96 committed blocks per step, more than
+    # the 64 threads of the refresh workgroup (Hkv * d = 64)
+    "f32_chain64_c1_c2": (synth.Workload("ms6", 1, 64, 1, 1, 64, "f32", (1, 2), 10, 1, 63, 1.0, 3006, prefix="raw"), 3),
 }
 
 
@@ -146,6 +149,7 @@ FUSED = {
     "f32_d64_c4_c16": (synth.Workload("fu2", 3, 7, 8, 2, 64, "f32", (4, 16), 13, 2, 3, 0.6, 3302, prefix="raw"), 30),
     "bf16_chain_c1_c4": (synth.Workload("fu3", 2, 8, 8, 1, 128, "bf16", (1, 4), 9, 1, 7, 0.9, 3303, prefix="raw"), 25),
     "bf16_chain_c8_c32": (synth.Workload("fu4", 2, 8, 16, 2, 128, "bf16", (8, 32), 250, 1, 7, 0.9, 3304, prefix="raw"), 25),
+    "f32_chain64_c1_c2": (synth.Workload("fu5", 1, 64, 1, 1, 64, "f32", (1, 2), 10, 1, 63, 1.0, 3305, prefix="raw"), 3),
 }
 
 

@@ -73,18 +73,19 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
     nc[l] = P2 / st.lvl[l].C - j0[l];
   }
   const int ncom = nc[0] + nc[1];
-  if (tid <= m && (sh.pth[tid] < 0 || sh.pth[tid] >= D)) atomicOr(&sh.bad, 1);
-  if (!full && tid < ncom) {
-    const bool l1 = tid >= nc[0];  // levels are picked by selection, not by a run-time index
+  if (tid <= m && (sh.pth[tid] < 0 || sh.pth[tid] >= D)) atomicOr(&sh.bad, 1);  // (m < D <= threads)
+  // (up to 2 (D + 1) blocks, more than the threads of a small workgroup)
+  for (int i = full ? ncom : tid; i < ncom; i += nt) {
+    const bool l1 = i >= nc[0];  // levels are picked by selection, not by a run-time index
     const tv_level& lv = l1 ? st.lvl[1] : st.lvl[0];
     const int C = lv.C;
-    const int j = l1 ? j0[1] + tid - nc[0] : j0[0] + tid;
+    const int j = l1 ? j0[1] + i - nc[0] : j0[0] + i;
     int page;
     if (!tile_page(lv, b, j >> 6, &page)) atomicOr(&sh.bad, 2);
-    sh.it_l[tid] = l1 ? 1 : 0;
-    sh.it_j[tid] = j;
-    sh.it_u[tid] = sh.pth[j * C + C - 1 - P];  // path node at the block's last position
-    sh.it_page[tid] = page;
+    sh.it_l[i] = l1 ? 1 : 0;
+    sh.it_j[i] = j;
+    sh.it_u[i] = sh.pth[j * C + C - 1 - P];  // path node at the block's last position
+    sh.it_page[i] = page;
   }
   __syncthreads();
   const int bad = sh.bad;
@@ -92,12 +93,13 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
     if (tid == 0) seq_err[b] = (bad & 1) ? TV_SEQ_BAD_PATH : full ? TV_SEQ_POOL_FULL : TV_SEQ_BAD_PAGE;
     return;
   }
-  if (commit_log != nullptr && tid < ncom) {
-    const int l = sh.it_l[tid];
-    int32_t* row = commit_log + (((size_t)b * L + l) * D + (sh.it_j[tid] - (l ? j0[1] : j0[0]))) * 2;
-    row[0] = sh.it_j[tid];
-    row[1] = sh.it_u[tid];
-  }
+  if (commit_log != nullptr)
+    for (int i = tid; i < ncom; i += nt) {
+      const int l = sh.it_l[i];
+      int32_t* row = commit_log + (((size_t)b * L + l) * D + (sh.it_j[i] - (l ? j0[1] : j0[0]))) * 2;
+      row[0] = sh.it_j[i];
+      row[1] = sh.it_u[i];
+    }
   const int leaf = sh.pth[m];
   // the finest level's raw tail: positions [t0, P2) come from the path; positions below
   // P keep their slot when no block closed (t_new == old start), when one closed t_new > P
