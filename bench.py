@@ -44,7 +44,7 @@ N_INPUT_SETS = 4        # distinct per-step input sets, rotated
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed steps first (kernel times drift for the first ~10 ms of a busy period)")
     ap.add_argument("--workload", default="high_batch")
@@ -116,7 +116,8 @@ PREFIX_KERNEL = "tv::k_attn_mfma<4, 1, false>"  # the contiguous-pool instance t
 
 
 def _counter_per_kernel(path: str, counter: str) -> dict:
-    """Mean counter value (KiB) per dispatch, by kernel name, from a rocprofv3 csv."""
+    """Mean value of a counter per dispatch (FETCH_SIZE / WRITE_SIZE: KiB; the derived
+    utilisation metrics: percent or a ratio), by kernel name, from a rocprofv3 csv."""
     import csv
     acc = {}
     with open(path) as fh:
@@ -209,7 +210,40 @@ def summarize_profiles(d: str, workload: str) -> None:
     lines += ["", f"Prefix kernel: {(rd + wr) / 1e9:.4f} GB of HBM traffic per launch against {alg / 1e9:.4f} GB "
               f"algorithmic: ratio {(rd + wr) / alg:.4f}.", ""]
     open(os.path.join(out_dir, f"hbm_bytes_{workload}.md"), "w").write("\n".join(lines))
+    util = os.path.join(d, "util", "run_counter_collection.csv")
+    if os.path.exists(util):
+        summarize_utilisation(util, workload, fl)
     print(json.dumps(rec))
+
+
+UTIL_METRICS = ("MfmaUtil", "VALUBusy", "LdsUtil", "LdsBankConflict")
+
+
+def summarize_utilisation(path: str, workload: str, bench_line: dict) -> None:
+    """The compute side of the prefix kernel from one rocprofv3 pass of derived metrics
+    (rocprofv3's own definitions): MFMA busy cycles per SIMD, VALU busy, LDS busy and LDS
+    bank conflicts per access, per kernel, as the committed summary."""
+    vals = {m: _counter_per_kernel(path, m) for m in UTIL_METRICS}
+    cmd = f"rocprofv3 --pmc {' '.join(UTIL_METRICS)} --output-format csv -d <dir> -o run -- {PROFILE_COUNTER_BENCH}"
+    kernels = sorted({k for v in vals.values() for k in v if "tv::" in k})
+    lines = [f"# Compute-side counters per dispatch: the verify step at {workload}", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmd, "",
+             "rocprofv3's derived metrics: MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) *",
+             "SIMDs); VALUBusy = 100 * sum(SQ_ACTIVE_INST_VALU) / CUs / max(GRBM_GUI_ACTIVE); LdsUtil = 100 *",
+             "sum(SQ_LDS_IDX_ACTIVE) / (max(GRBM_GUI_ACTIVE) * CUs); LdsBankConflict = conflict cycles per",
+             "conflict-free LDS cycle.", "",
+             "| kernel | MfmaUtil % | VALUBusy % | LdsUtil % | LdsBankConflict |", "|---|---|---|---|---|"]
+    for k in kernels:
+        lines.append(f"| `{k.split('(')[0].replace('void ', '')}` | " +
+                     " | ".join(f"{vals[m].get(k, float('nan')):.3g}" for m in UTIL_METRICS) + " |")
+    flops = 4.0 * bench_line["config"]["B"] * bench_line["config"]["Hq"] * bench_line["config"]["D"] * \
+        bench_line["config"]["head_dim"] * bench_line["roofline"]["algorithmic_bytes_per_launch"] / \
+        (bench_line["config"]["B"] * bench_line["config"]["Hkv"] * bench_line["config"]["head_dim"] * 4.0)
+    lines += ["", f"Algorithmic MFMA work of the prefix kernel at this shape: about {flops / 1e12:.3f} TFLOP per launch "
+              f"(4 * B * Hq * D * d per committed entry), {flops / (bench_line['roofline']['avg_launch_ms'] * 1e-3) / 1e12:.0f} "
+              "TFLOP/s at the launch time of the same run, against 2500 TFLOP/s dense bf16: the kernel is bound by HBM, "
+              "and the matrix cores are busy for the share of cycles shown.", ""]
+    open(os.path.join(ROOT, "profiles", f"utilisation_{workload}.md"), "w").write("\n".join(lines))
 
 
 SWEEP_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/b{B} -o run -- "
