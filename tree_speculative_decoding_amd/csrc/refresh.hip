@@ -22,7 +22,10 @@ namespace tv {
 struct RefreshLds {
   static constexpr int kMaxCommits = 2 * (TV_MAX_D + 1);  // per level at most (m + 1)/C + 1
   int pth[TV_MAX_D];
-  int it_l[kMaxCommits], it_j[kMaxCommits], it_u[kMaxCommits], it_page[kMaxCommits];
+  int it_l[kMaxCommits], it_j[kMaxCommits], it_u[kMaxCommits];
+  // element offset of the block's tile for KV head 0, and from one head's tile to the
+  // next (tile_offset is linear in the head in every pool layout)
+  size_t it_tile0[kMaxCommits], it_gstep[kMaxCommits];
   int bad;
 };
 
@@ -82,10 +85,13 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
     const int j = l1 ? j0[1] + i - nc[0] : j0[0] + i;
     int page;
     if (!tile_page(lv, b, j >> 6, &page)) atomicOr(&sh.bad, 2);
+    const bool paged = lv.page_table != nullptr;
+    const size_t t0 = tile_offset(paged, page, lv.cap, st.B, Hkv, d, b, 0, j >> 6);
     sh.it_l[i] = l1 ? 1 : 0;
     sh.it_j[i] = j;
     sh.it_u[i] = sh.pth[j * C + C - 1 - P];  // path node at the block's last position
-    sh.it_page[i] = page;
+    sh.it_tile0[i] = t0;
+    sh.it_gstep[i] = tile_offset(paged, page, lv.cap, st.B, Hkv, d, b, 1, j >> 6) - t0;
   }
   __syncthreads();
   const int bad = sh.bad;
@@ -157,7 +163,7 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
         if (c0 + t < ncom) {  // uniform
           const int i = c0 + t, j = sh.it_j[i];
           const tv_level& lv = sh.it_l[i] != 0 ? st.lvl[1] : st.lvl[0];
-          const size_t tb = tile_offset(lv.page_table != nullptr, sh.it_page[i], lv.cap, st.B, Hkv, d, b, g, j >> 6);
+          const size_t tb = sh.it_tile0[i] + (size_t)g * sh.it_gstep[i];
           Bits<T>::st((T*)lv.k, tb + (size_t)(j & 63) * d + dd, ck[t]);
           Bits<T>::st((T*)lv.vt, tb + (size_t)dd * 64 + (j & 63), cv[t]);
         }
