@@ -891,9 +891,11 @@ def cpu_baseline(w, budget_s: float):
     import synth
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ",".join(sorted({str(i.get("internal_api")) for i in info if i.get("user_api") == "blas"})) or "none"
     except Exception:
-        threads = 1
+        threads, blas = 1, "unknown"
     caps = [w.P // C + 64 for C in w.levels]
     done, t_used = 0, 0.0
     b = 0
@@ -909,7 +911,7 @@ def cpu_baseline(w, budget_s: float):
         t_used += time.perf_counter() - t0
         done += 1
         b += 1
-    return {"value": round(done * w.D / t_used, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done * w.D / t_used, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle", "blas": blas,
             "sample": f"{done} of {w.B} sequences of {w.name}, one full step each (plan, attention, scratch, "
                       f"accept, refresh), fp64 numpy; input widening excluded; {t_used:.1f} s"}
 
