@@ -551,7 +551,7 @@ def main():
         ceiling["attn_frac_of_ceiling"] = round(achieved / ceiling["GB/s"], 4)
         result["read_ceiling"] = ceiling
         result["draft_tree"] = time_draft_tree(w, args.steps, stream)
-        result["draft_attn"] = time_draft_attn(w, st, stream, reps=3)
+        result["draft_attn"] = time_draft_attn(w, st, stream, reps=10)
         result["paged_pool"] = time_paged(w, st, stream, reps=5)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
@@ -780,12 +780,17 @@ def time_draft_tree(w, steps: int, stream) -> dict:
             "bound": "latency (one workgroup per sequence; E rows of the vocabulary each)"}
 
 
+DRAFT_WARM_LAUNCHES = 40  # untimed launches ahead of the draft-attention and paged timings
+PAGED_ROUNDS = 4
+
+
 def time_draft_attn(w, st, stream, reps: int) -> dict:
     """Draft-decode reuse of the branch-aware attention: for each level t of the
     workload's expansion (top-k, draft steps), tv_draft_attn over the 1 + k + ... +
     k^(t-1) nodes created so far, with one plan of the whole expansion shared by the
-    levels; each launch is timed with fence-free events on `stream` (`reps` per level).
-    Synthetic Q / tree K/V of the workload's dtype; the state is the benchmark's."""
+    levels; after DRAFT_WARM_LAUNCHES untimed launches, `reps` launches back to back, each
+    timed with fence-free events on `stream`.  Synthetic Q / tree K/V of the workload's
+    dtype; the state is the benchmark's."""
     import torch
     import synth
     import tree_speculative_decoding_amd as tv
@@ -814,7 +819,10 @@ def time_draft_attn(w, st, stream, reps: int) -> dict:
         out = torch.empty(w.B, D, w.Hq, w.d, dtype=qd.dtype, device="cuda")
         ws = torch.empty(tv.tv_verify_attn_workspace_bytes(D, w.Hq, st) // 4 + 64, dtype=torch.float32,
                          device="cuda")
-        tv.tv_draft_attn(qd, kd, vd, anc, err, st, out, None, ws, stream=stream)  # warm-up
+        # untimed launches first (the clock settles ~10 ms into a busy period), then the
+        # timed ones queued right behind them
+        for _ in range(DRAFT_WARM_LAUNCHES):
+            tv.tv_draft_attn(qd, kd, vd, anc, err, st, out, None, ws, stream=stream)
         ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
         for a_, b_ in ev:
             tv.tv_set_timing_events(a_, b_)
@@ -833,8 +841,9 @@ def time_draft_attn(w, st, stream, reps: int) -> dict:
 
 def time_paged(w, st, stream, reps: int) -> dict:
     """Gather cost of a paged pool: the benchmark's state copied into 64-entry pages at
-    random physical positions, then `reps` verify launches on each of the contiguous and
-    the paged state, alternating (same inputs, no refresh, so both stay equal)."""
+    random physical positions; after untimed launches, PAGED_ROUNDS rounds of `reps`
+    back-to-back verify launches on the contiguous and then the paged state (same inputs,
+    no refresh, so both stay equal)."""
     import torch
     import synth
     import tree_speculative_decoding_amd as tv
@@ -862,16 +871,21 @@ def time_paged(w, st, stream, reps: int) -> dict:
     tv.tv_build_tree_mask(i32(s.parents), anc, depth, err, stream)
     out = [torch.empty(w.B, w.D, w.Hq, w.d, dtype=q.dtype, device="cuda") for _ in range(2)]
     ws = torch.empty(tv.tv_verify_attn_workspace_bytes(w.D, w.Hq, st) // 4 + 64, dtype=torch.float32, device="cuda")
-    ms = {0: [], 1: []}
-    for i in range(reps + 1):
+    # untimed launches first, then blocks of `reps` back-to-back launches of each state,
+    # alternating, all queued without a synchronisation in between
+    for _ in range(DRAFT_WARM_LAUNCHES):
+        tv.tv_verify_attn(q, kt, vt, anc, depth, err, st, None, out[0], None, ws, 0, stream)
+    ev = {0: [], 1: []}
+    for _ in range(PAGED_ROUNDS):
         for which, state in ((0, st), (1, sp)):
-            a_, b_ = TimingEvent(), TimingEvent()
-            tv.tv_set_timing_events(a_, b_)
-            tv.tv_verify_attn(q, kt, vt, anc, depth, err, state, None, out[which], None, ws, 0, stream)
-            tv.tv_set_timing_events(None, None)
-            torch.cuda.synchronize()
-            if i > 0:  # the first round warms up
-                ms[which].append(a_.elapsed_ms(b_))
+            for _ in range(reps):
+                a_, b_ = TimingEvent(), TimingEvent()
+                tv.tv_set_timing_events(a_, b_)
+                tv.tv_verify_attn(q, kt, vt, anc, depth, err, state, None, out[which], None, ws, 0, stream)
+                ev[which].append((a_, b_))
+    tv.tv_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    ms = {k: [a_.elapsed_ms(b_) for a_, b_ in v] for k, v in ev.items()}
     same = bool(torch.equal(out[0].view(torch.int16), out[1].view(torch.int16))) if w.dtype == "bf16" else \
         bool(torch.equal(out[0], out[1]))
     c, p_ = float(np.mean(ms[0])) * 1e3, float(np.mean(ms[1])) * 1e3
