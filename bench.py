@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--summarize-sweep-traces", default="", metavar="DIR",
                     help="write profiles/step_long_context_kernel_trace.md from rocprofv3 kernel-trace csv "
                          "runs of the sweep, one per batch size, in DIR/b<B>/")
+    ap.add_argument("--summarize-step-trace", default="", metavar="DIR",
+                    help="write profiles/step_<workload>_kernel_trace.md from a rocprofv3 kernel-trace csv run "
+                         "of the STEP_TRACE_CMD command in DIR/")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (to scale HBM byte counters)")
     return ap.parse_args()
@@ -248,6 +251,35 @@ def summarize_utilisation(path: str, workload: str, bench_line: dict) -> None:
 
 SWEEP_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/b{B} -o run -- "
                    "python3 bench.py --sweep <dir>/b{B}.md --sweep-batches {B} --steps 20 --warmup 5")
+
+
+STEP_TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                  "python3 bench.py --workload {W} --steps 100 --warmup 40 --no-cpu-baseline --no-extras")
+
+
+def summarize_step_trace(d: str, workload: str) -> None:
+    """Per-kernel launch statistics of one workload's steps (rocprofv3 kernel trace of the
+    STEP_TRACE_CMD run in d): every kernel of the step with its share of the step, as the
+    committed summary."""
+    import csv
+    line = json.loads([l for l in open(os.path.join(d, "run.txt")).read().splitlines() if l.startswith("{")][-1])
+    cfg = line["config"]
+    rows = [r for r in csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))) if "tv::" in r["Name"]]
+    calls = max(int(r["Calls"]) for r in rows)
+    lines = [f"# Kernel-trace summary: the verify step at {workload} (B={cfg['B']}, D={cfg['D']}, "
+             f"{cfg['Hq']}/{cfg['Hkv']} heads, d={cfg['head_dim']}, {line['dtype']}, {cfg['prefix_tokens']}-token "
+             f"prefix, tree {cfg['tree']})", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", "    " + STEP_TRACE_CMD.format(W=workload), "",
+             f"Per-kernel statistics over every step of the run (untimed settling steps, then the timed ones: {calls} "
+             "launches of each kernel).  The profiler adds its own overhead per launch;",
+             f"the bench line of the same run: {line['ms_per_step'] * 1e3:.1f} us per step, verify launch "
+             f"{line['roofline']['avg_launch_ms'] * 1e3:.1f} us (HIP events).", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+    lines.append("")
+    open(os.path.join(ROOT, "profiles", f"step_{workload}_kernel_trace.md"), "w").write("\n".join(lines))
 
 
 def summarize_sweep_traces(d: str) -> None:
@@ -449,6 +481,9 @@ def main():
         return
     if args.summarize_sweep_traces:
         summarize_sweep_traces(args.summarize_sweep_traces)
+        return
+    if args.summarize_step_trace:
+        summarize_step_trace(args.summarize_step_trace, args.workload)
         return
     if args.sweep:
         sweep(args)
