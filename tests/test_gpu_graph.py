@@ -1,7 +1,7 @@
-"""The four calls of a step (plan, verify attention with the scratch pad, accept, refresh)
-captured once in a HIP graph and replayed: the library allocates nothing, synchronises
-nothing and records no memset inside the calls, so a replay must equal the eager step bit
-for bit.  Each replay starts from the same restored state, with eager work and a
+"""The calls of a step (plan, verify attention with the scratch pad, accept and refresh as
+two calls or as tv_accept_refresh) captured once in a HIP graph and replayed: the library
+allocates nothing, synchronises nothing and records no memset inside the calls, so a
+replay must equal the eager step bit for bit.  Each replay starts from the same restored state, with eager work and a
 synchronisation between replays, and every replay is compared with the eager result
 (outputs, acceptance, commit log and the refreshed state)."""
 import sys
@@ -56,21 +56,25 @@ CASES = {
                                    prefix="raw"), 37),
     # the vector path (fp32) with its tail and chain in the finish kernel
     "f32": (synth.Workload("g3", 2, 6, 8, 2, 64, "f32", (4, 16), 611, 2, 3, 0.6, 5003, prefix="raw"), 0),
+    # paged pools (random page table), split units
+    "paged": (synth.Workload("g4", 3, 8, 64, 8, 128, "bf16", (4, 128), 1500 + 2, 2, 3, 0.7, 5004, prefix="raw"), 29),
 }
+PAGE_SEEDS = {"paged": 77}
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["four_calls", "fused_accept_refresh"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_graph_replay_equals_eager(name):
+def test_graph_replay_equals_eager(name, fused):
     import torch
     w, parts = CASES[name]
-    _say(f"graph replay {name}")
+    _say(f"graph replay {name} fused={fused}")
     caps = pooled_caps(w, 64)
-    st = device_state(w, caps, poison=True)
+    st = device_state(w, caps, poison=True, page_seed=PAGE_SEEDS.get(name), spare_pages=3 if name in PAGE_SEEDS else 0)
     r = Runner(st, w.D, w.Hq, parts)
     x = upload_step(synth.step_inputs(w, 0), w.dtype)
     snap = _snapshot(st)
 
-    r.step(x)  # eager reference (also loads every kernel before capture)
+    r.step(x, fused=fused)  # eager reference (also loads every kernel before capture)
     torch.cuda.synchronize()
     ref = [t.clone() for t in _results(r, st)]
 
@@ -78,7 +82,7 @@ def test_graph_replay_equals_eager(name):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        r.step(x)
+        r.step(x, fused=fused)
     torch.cuda.synchronize()
     for rep in range(3):
         _restore(st, snap)
