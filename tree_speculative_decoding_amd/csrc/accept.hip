@@ -15,8 +15,7 @@ __global__ __launch_bounds__(256) void k_accept(int B, int D, const int32_t* __r
                                                 int32_t* __restrict__ bonus) {
   const int b = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (b >= B) return;
-  const int err = seq_err != nullptr ? seq_err[b] : TV_SEQ_OK;
-  accept_one(b, D, parents, anc, depth, draft, target, err, m_out, path, bonus, nullptr);
+  accept_one(b, D, parents, anc, depth, draft, target, seq_err, m_out, path, bonus, nullptr);
 }
 
 hipError_t launch_accept(int B, int D, const int32_t* parents, const uint64_t* anc,

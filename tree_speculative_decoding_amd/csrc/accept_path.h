@@ -13,18 +13,31 @@
 
 namespace tv {
 
-// Sequence b's acceptance.  err is the sequence's status: a flagged sequence gets m = -1,
-// bonus = -1 and an all -1 path.  Writes path[b][0..D), m_out[b] and bonus[b]; when pth
+// Sequence b's acceptance.  seq_err (may be NULL) holds the sequences' status: a flagged
+// sequence gets m = -1, bonus = -1 and an all -1 path.  Writes path[b][0..D), m_out[b] and bonus[b]; when pth
 // is not NULL (LDS, D entries) the path is also written there.  Returns m to every lane.
 __device__ __forceinline__ int accept_one(int b, int D, const int32_t* __restrict__ parents,
                                           const uint64_t* __restrict__ anc, const int32_t* __restrict__ depth,
                                           const int32_t* __restrict__ draft, const int32_t* __restrict__ target,
-                                          int err, int32_t* __restrict__ m_out, int32_t* __restrict__ path,
+                                          const int32_t* __restrict__ seq_err, int32_t* __restrict__ m_out,
+                                          int32_t* __restrict__ path,
                                           int32_t* __restrict__ bonus, int* pth) {
   const int lane = threadIdx.x & 63;
   const size_t base = (size_t)b * D;
   const bool live = lane < D;
-  if (err != TV_SEQ_OK) {
+  // every load at once, ahead of the status test: the node's chain, depth, parent, draft
+  // token and target token (its parent's target and the bonus then come from their lanes)
+  uint64_t a = 0;
+  int dep = 0, par = -1, dr = 0, tg = -1;
+  if (live) {
+    a = anc[base + lane] & node_mask(D);
+    dep = depth[base + lane];
+    par = parents[base + lane];
+    dr = draft[base + lane];
+    tg = target[base + lane];
+  }
+  const int err = seq_err != nullptr ? seq_err[b] : TV_SEQ_OK;
+  if (err != TV_SEQ_OK) {  // wave-uniform
     if (live) {
       path[base + lane] = -1;
       if (pth != nullptr) pth[lane] = -1;
@@ -35,19 +48,9 @@ __device__ __forceinline__ int accept_one(int b, int D, const int32_t* __restric
     }
     return -1;
   }
-  bool match = false;
-  uint64_t a = 0;
-  int dep = 0;
-  if (live) {
-    a = anc[base + lane] & node_mask(D);
-    dep = depth[base + lane];
-    if (lane == 0) {
-      match = true;
-    } else {
-      const int p = parents[base + lane];
-      match = p >= 0 && p < D && draft[base + lane] == target[base + p];
-    }
-  }
+  const bool par_ok = par >= 0 && par < D;
+  const int tpar = __shfl(tg, par_ok ? par : 0, 64);
+  const bool match = live && (lane == 0 || (par_ok && dr == tpar));
   const uint64_t matched = __ballot(match);
   const bool accepted = live && (a & ~matched) == 0ull;
   // key: deeper wins, then smaller index; root (depth 0, index 0) always qualifies
@@ -66,9 +69,10 @@ __device__ __forceinline__ int accept_one(int b, int D, const int32_t* __restric
       if (pth != nullptr) pth[lane] = -1;
     }
   }
+  const int bon = __shfl(tg, leaf, 64);
   if (lane == 0) {
     m_out[b] = m;
-    bonus[b] = target[base + leaf];
+    bonus[b] = bon;
   }
   return m;
 }

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(1024) void k_accept_refresh(int D, tv_state st, tv_
   const int P = st.P[b];
   if (tid < 64) {  // the first wave: every path slot -1, then the accepted path
     if (tid < D) sh.pth[tid] = -1;
-    const int m = accept_one(b, D, parents, anc, depth, draft, target, err, m_out, path, bonus, sh.pth);
+    const int m = accept_one(b, D, parents, anc, depth, draft, target, seq_err, m_out, path, bonus, sh.pth);
     if (tid == 0) {
       m_s = m;
       sh.bad = 0;
