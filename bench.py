@@ -309,7 +309,7 @@ def summarize_sweep_traces(d: str) -> None:
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("attn_mfma.hip", "tv_common.h"):
+    for f in ("attn_mfma.hip", "scratch_pad.h", "tv_common.h"):
         with open(os.path.join(ROOT, "tree_speculative_decoding_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

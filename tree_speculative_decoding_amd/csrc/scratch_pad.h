@@ -41,6 +41,29 @@ template <> struct Quad<uint16_t> {
   }
 };
 
+// Four consecutive elements as raw bits (8 or 16 bytes), widened to fp32 after the wait.
+template <typename T> struct QuadRaw;
+template <> struct QuadRaw<float> {
+  using type = float4;
+  static __device__ __forceinline__ float4 load(const float* p, size_t i) { return *(const float4*)(p + i); }
+  static __device__ __forceinline__ float4 widen(float4 r) { return r; }
+  static __device__ __forceinline__ void pin(float4 r) { asm volatile("" ::"v"(r.x), "v"(r.y), "v"(r.z), "v"(r.w)); }
+};
+template <> struct QuadRaw<uint16_t> {
+  using type = uint2;
+  static __device__ __forceinline__ uint2 load(const uint16_t* p, size_t i) { return *(const uint2*)(p + i); }
+  static __device__ __forceinline__ float4 widen(uint2 r) {
+    return make_float4(bf16_bits_to_f32(r.x & 0xffffu), bf16_bits_to_f32(r.x >> 16),
+                       bf16_bits_to_f32(r.y & 0xffffu), bf16_bits_to_f32(r.y >> 16));
+  }
+  static __device__ __forceinline__ void pin(uint2 r) { asm volatile("" ::"v"(r.x), "v"(r.y)); }
+};
+
+// c ? a : b per component (a select of whole float4 structs is compiled through memory)
+__device__ __forceinline__ float4 sel4(bool c, float4 a, float4 b) {
+  return make_float4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
 __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
@@ -72,60 +95,77 @@ __device__ __forceinline__ void scratch_node(const AttnArgs& a, int b, int i, in
   const T* vt = (const T*)a.v_tree;
   const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 
+  using R = QuadRaw<T>;
+  static_assert(TV_MAX_LEVELS == 2, "two levels: the sums below are named per level");
+  const bool lv1 = a.n_levels > 1;
   for (int e = 4 * tid; e < HD; e += 4 * 256) {
-    float4 sk[TV_MAX_LEVELS], sv[TV_MAX_LEVELS];
-#pragma unroll
-    for (int l = 0; l < TV_MAX_LEVELS; ++l) {
-      const bool use_open = l < a.n_levels && b0[l] < P;
-      const size_t so = (size_t)b * HD + e;
-      sk[l] = use_open ? *(const float4*)(a.open_k[l] + so) : z;
-      sv[l] = use_open ? *(const float4*)(a.open_v[l] + so) : z;
-    }
+    // the open sums (level 0's address where level 1 is absent) and the chain's first
+    // batch, loaded unconditionally and held as raw bits until every load is out (a
+    // selected load is otherwise moved into a branch that waits for it there)
+    const size_t so = (size_t)b * HD + e;
+    float4 sk0 = *(const float4*)(a.open_k[0] + so), sv0 = *(const float4*)(a.open_v[0] + so);
+    float4 sk1 = *(const float4*)(a.open_k[lv1 ? 1 : 0] + so), sv1 = *(const float4*)(a.open_v[lv1 ? 1 : 0] + so);
     // the chain, root first, kBatch nodes at a time: every load of a batch, then the
     // additions in chain order
     uint64_t mm = chain;
-    while (mm != 0ull) {
+    bool first = true;
+    do {
       int js[kBatch];
+      typename R::type kr[kBatch], vr[kBatch];
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
         js[t] = mm != 0ull ? __builtin_ctzll(mm) : -1;
         if (mm != 0ull) mm &= mm - 1ull;
       }
-      float4 kk[kBatch], vv[kBatch];
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
         const size_t o = ((size_t)b * a.D + (js[t] >= 0 ? js[t] : 0)) * HD + e;
-        kk[t] = js[t] >= 0 ? Quad<T>::load(kt, o) : z;
-        vv[t] = js[t] >= 0 ? Quad<T>::load(vt, o) : z;
+        kr[t] = R::load(kt, o);
+        vr[t] = R::load(vt, o);
+      }
+#pragma unroll
+      for (int t = 0; t < kBatch; ++t) {
+        R::pin(kr[t]);
+        R::pin(vr[t]);
+      }
+      if (first) {  // the committed open sums count only where the block began before the tree
+        const bool open0 = b0[0] < P, open1 = lv1 && b0[1] < P;
+        sk0 = sel4(open0, sk0, z);
+        sv0 = sel4(open0, sv0, z);
+        sk1 = sel4(open1, sk1, z);
+        sv1 = sel4(open1, sv1, z);
+        first = false;
       }
 #pragma unroll
       for (int t = 0; t < kBatch; ++t) {
         if (js[t] < 0) continue;  // (the rest of the batch is empty too)
         const int pj = P + dep_s[js[t]];
-#pragma unroll
-        for (int l = 0; l < TV_MAX_LEVELS; ++l)
-          if (l < a.n_levels && pj >= b0[l]) {
-            sk[l] = add4(sk[l], kk[t]);
-            sv[l] = add4(sv[l], vv[t]);
-          }
+        const float4 kk = R::widen(kr[t]), vv = R::widen(vr[t]);
+        if (pj >= b0[0]) {
+          sk0 = add4(sk0, kk);
+          sv0 = add4(sv0, vv);
+        }
+        if (lv1 && pj >= b0[1]) {
+          sk1 = add4(sk1, kk);
+          sv1 = add4(sv1, vv);
+        }
       }
-    }
+    } while (mm != 0ull);
 #pragma unroll
     for (int l = 0; l < TV_MAX_LEVELS; ++l) {
       if (l >= a.n_levels) continue;
+      const float4 ks = sel4(l != 0, sk1, sk0), vs = sel4(l != 0, sv1, sv0);  // (l is a constant here)
       const int C = a.C[l];
       const size_t dst = ((size_t)b * a.D + i) * HD + e;
       if ((pos + 1) % C == 0) {
         const float cf = (float)C;
-        Quad<T>::store((T*)a.scratch.entry_k[l], dst,
-                       make_float4(sk[l].x / cf, sk[l].y / cf, sk[l].z / cf, sk[l].w / cf));
-        Quad<T>::store((T*)a.scratch.entry_v[l], dst,
-                       make_float4(sv[l].x / cf, sv[l].y / cf, sv[l].z / cf, sv[l].w / cf));
+        Quad<T>::store((T*)a.scratch.entry_k[l], dst, make_float4(ks.x / cf, ks.y / cf, ks.z / cf, ks.w / cf));
+        Quad<T>::store((T*)a.scratch.entry_v[l], dst, make_float4(vs.x / cf, vs.y / cf, vs.z / cf, vs.w / cf));
         *(float4*)(a.scratch.open_k[l] + dst) = z;
         *(float4*)(a.scratch.open_v[l] + dst) = z;
       } else {
-        *(float4*)(a.scratch.open_k[l] + dst) = sk[l];
-        *(float4*)(a.scratch.open_v[l] + dst) = sv[l];
+        *(float4*)(a.scratch.open_k[l] + dst) = ks;
+        *(float4*)(a.scratch.open_v[l] + dst) = vs;
       }
     }
   }
