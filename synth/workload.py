@@ -80,12 +80,14 @@ def _mk(name, B, D, Hq, Hkv, d, dtype, levels, P, topk, steps, p, seed, prefix="
 
 
 #: The named workloads.  Tiny is the small fp32 parity case; High batch is the
-#: throughput workload (B=64, D=8, 64/8 heads, d=128, bf16, 32768-token prefix).
+#: throughput workload (B=64, D=8, 64/8 heads, d=128, bf16, 32768-token prefix); wide_tree
+#: is the same batch with a 16-node tree (top-k 2, 4 steps), 128 query rows per KV head.
 WORKLOADS: Dict[str, Workload] = {
     "tiny": _mk("tiny", 1, 6, 4, 1, 64, "f32", (4,), 256, 2, 3, 0.6, 1000, prefix="raw"),
     "linear": _mk("linear", 8, 8, 64, 8, 128, "bf16", (4, 128), 4096, 1, 7, 0.7, 1001),
     "tree": _mk("tree", 4, 6, 64, 8, 128, "bf16", (4, 128), 8192, 2, 3, 0.5, 1002),
     "high_batch": _mk("high_batch", 64, 8, 64, 8, 128, "bf16", (4, 128), 32768, 2, 3, 0.6, 1003),
+    "wide_tree": _mk("wide_tree", 64, 16, 64, 8, 128, "bf16", (4, 128), 32768, 2, 4, 0.6, 1004),
 }
 
 

@@ -29,10 +29,10 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
   T* kt_s = (T*)lds_raw;                         // [D][DH]
   T* vt_s = kt_s + (size_t)a.D * DH;             // [D][DH]
 
-  constexpr int kGroups = 64 / kFinishWaves;     // workgroups per 64-row block
+  const int groups = a.unit_rows / kFinishWaves;  // workgroups per unit's rows
   const int g = blockIdx.x % a.Hkv;
-  const int rb = blockIdx.x / a.Hkv / kGroups;
-  const int rg = blockIdx.x / a.Hkv % kGroups;
+  const int rb = blockIdx.x / a.Hkv / groups;
+  const int rg = blockIdx.x / a.Hkv % groups;
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const size_t bg = (size_t)b * a.Hkv + g;
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
   const uint64_t nodes = node_mask(a.D);
   const T* q = (const T*)a.q;
   {
-    const int r = rb * 64 + rg * kFinishWaves + w;
+    const int r = rb * a.unit_rows + rg * kFinishWaves + w;
     if (r >= a.R) return;  // wave-uniform; no barrier follows
     const int i = r / a.G, hh = r - i * a.G, h = g * a.G + hh;
     const size_t obase = (((size_t)b * a.D + i) * a.Hq + h) * DH + lane * EPL;
@@ -215,7 +215,7 @@ static hipError_t launch_finish_t(const AttnArgs& a, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(a.Hkv * a.row_blocks * (64 / kFinishWaves), a.B), block(kFinishWaves * 64);
+  dim3 grid(a.Hkv * a.row_blocks * (a.unit_rows / kFinishWaves), a.B), block(kFinishWaves * 64);
   hipLaunchKernelGGL((k_attn_finish<T, DH>), grid, block, lds, s, a);
   return hipGetLastError();
 }

@@ -72,8 +72,10 @@ static __device__ __attribute__((aligned(256))) uint4 g_zero_chunk[1024];
 // the number of 16-entry tiles the tail + tree chunk takes (its registers are sized by it);
 // PAGED selects paged pools (a page-table read per chunk) over contiguous ones.
 template <int NW, int TT, bool PAGED>
-__global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs a) {
+  static_assert(NW == 4 || NW == 8, "4 waves (64-row units, two workgroups per CU) or 8 (128-row units, one)");
   constexpr int NT = NW * 64;
+  constexpr int kUnitRows = 16 * NW;          // query rows of a unit: 16 per wave
   constexpr int PER = (1024 + NT - 1) / NT;   // K pieces (and V pieces) per thread
   constexpr bool kFull = 1024 % NT == 0;
   static_assert(TT >= 1 && TT <= 4, "the tail + tree chunk is at most 64 entries");
@@ -87,13 +89,15 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, grp = lane >> 4;
-  if ((int)blockIdx.x < a.fold_scratch) {  // a scratch-pad workgroup (uniform)
+  if (NW == 4 && (int)blockIdx.x < a.fold_scratch) {  // a scratch-pad workgroup (uniform; 256 threads)
     const int sb = blockIdx.x / a.D;
     scratch_node<uint16_t, 4>(a, sb, blockIdx.x - sb * a.D, (int*)smem);  // (4: no spill beside the stream's registers)
     return;
   }
   const int part = blockIdx.x - a.fold_scratch;  // this workgroup's slice of the stream
-  uint4 kpa[PER], vpa[PER], kpb[PER], vpb[PER];  // two chunks of loads in flight
+  // two chunks of loads in flight (8 waves: a third measured nothing, the LDS reads of 8
+  // waves per chunk bound that instance)
+  uint4 kpa[PER], vpa[PER], kpb[PER], vpb[PER];
 
   // this workgroup's slice of the units' chunks, laid end to end
   const long long total = a.units * a.tmax;
@@ -111,10 +115,10 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn_mfma(AttnArgs a) {
     const size_t bg = (size_t)b * a.Hkv + g;
 
     // Q^T operand: lane (n16, grp), k-step ks holds Q[row][32ks + 8grp .. +7]
-    const int row = rb * 64 + w * 16 + n16;
+    const int row = rb * kUnitRows + w * 16 + n16;
     const int node = row < a.R ? row / a.G : 0;
     const int head = g * a.G + (row - node * a.G);
-    const bool wave_has_rows = rb * 64 + w * 16 < a.R;  // wave-uniform
+    const bool wave_has_rows = rb * kUnitRows + w * 16 < a.R;  // wave-uniform
     bf16x8 qop[4];
     {
       const uint16_t* q = (const uint16_t*)a.q;
@@ -508,14 +512,25 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.parts == 0) return hipSuccess;
   const int tt = a.fused_tree ? a.tree_tiles : 1;
   const bool paged = a.pt[0] != nullptr;  // every level or none
-  if (paged) {
-    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, true>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
-    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, true>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_mfma<4, 4, true>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
+  const dim3 grid(a.parts + a.fold_scratch);
+  if (a.unit_rows == 128) {  // 8 waves, one workgroup per CU (no folded scratch workgroups)
+    if (paged) {
+      if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<8, 1, true>), grid, dim3(512), 0, s, a);
+      else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<8, 2, true>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((k_attn_mfma<8, 4, true>), grid, dim3(512), 0, s, a);
+    } else {
+      if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<8, 1, false>), grid, dim3(512), 0, s, a);
+      else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<8, 2, false>), grid, dim3(512), 0, s, a);
+      else hipLaunchKernelGGL((k_attn_mfma<8, 4, false>), grid, dim3(512), 0, s, a);
+    }
+  } else if (paged) {
+    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, true>), grid, dim3(256), 0, s, a);
+    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_mfma<4, 4, true>), grid, dim3(256), 0, s, a);
   } else {
-    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, false>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
-    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, false>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_mfma<4, 4, false>), dim3(a.parts + a.fold_scratch), dim3(256), 0, s, a);
+    if (tt == 1) hipLaunchKernelGGL((k_attn_mfma<4, 1, false>), grid, dim3(256), 0, s, a);
+    else if (tt == 2) hipLaunchKernelGGL((k_attn_mfma<4, 2, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_mfma<4, 4, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

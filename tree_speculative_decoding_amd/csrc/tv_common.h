@@ -136,7 +136,8 @@ struct AttnArgs {
   // sequence's committed entries are empty).  The units' chunks, laid end to end, are cut
   // into `parts` equal slices of `per` chunks, one workgroup each; a workgroup writes one
   // partial per unit its slice touches, in slot (workgroup - first workgroup of the unit).
-  int row_blocks;                    // RB = ceil(R / 64)
+  int unit_rows;                     // query rows of a unit: 64, or 128 for the 8-wave MFMA instance
+  int row_blocks;                    // RB = ceil(R / unit_rows)
   int tmax;                          // chunks per unit
   long long units;                   // B * Hkv * RB
   int parts;                         // workgroups of the prefix stream

@@ -88,7 +88,7 @@ int device_cus() {
 }
 
 struct Plan {
-  int R, row_blocks, tmax, parts, smax;
+  int R, unit_rows, row_blocks, tmax, parts, smax;
   long long units, per;
   size_t ws_o_bytes, ws_ml_off, total;
   bool fold;  // the MFMA prefix launch has room for the scratch pad's B*D workgroups
@@ -104,7 +104,12 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   Plan p{};
   const int G = Hq / st->Hkv;
   p.R = G * D;
-  p.row_blocks = (p.R + 63) / 64;
+  // the MFMA kernel takes more than 64 rows of a KV head (G*D > 64) in 128-row units of an
+  // 8-wave workgroup, one per CU, so the rows share one stream of the prefix; the vector
+  // kernel and smaller trees use 64-row units
+  const bool mfma = st->dtype == TV_BF16 && st->d == 128;
+  p.unit_rows = mfma && p.R > 64 ? 128 : 64;
+  p.row_blocks = (p.R + p.unit_rows - 1) / p.unit_rows;
   p.tmax = 0;
   for (int l = 0; l < st->n_levels; ++l) p.tmax += (st->lvl[l].cap + 63) / 64;
   p.units = (long long)st->B * st->Hkv * p.row_blocks;
@@ -115,20 +120,21 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
     p.smax = 0;
   } else {
     long long want;
-    const long long slots = (long long)device_cus() * 2;  // workgroups resident at once
-    const long long pad = (long long)st->B * D;             // scratch-pad workgroups
+    const bool wide = p.unit_rows == 128;
+    const long long slots = (long long)device_cus() * (wide ? 1 : 2);  // workgroups resident at once
+    const long long pad = (long long)st->B * D;                        // scratch-pad workgroups
     if (num_parts > 0) {
       want = num_parts;
-      p.fold = want + pad <= slots;
+      p.fold = !wide && want + pad <= slots;
     } else {
       want = slots;
       const long long by_size = (total + 3) / 4;
       if (want > by_size) want = by_size;
-      // the scratch pad rides in the same launch when the stream leaves room for it, or
-      // when it is a handful of workgroups (taken from the stream's)
-      if (want + pad <= slots) {
+      // the scratch pad rides in the same launch (of 256-thread workgroups) when the stream
+      // leaves room for it, or when it is a handful of workgroups (taken from the stream's)
+      if (!wide && want + pad <= slots) {
         p.fold = true;
-      } else if (pad <= 16 && pad < want) {
+      } else if (!wide && pad <= 16 && pad < want) {
         want = slots - pad;
         p.fold = true;
       }
@@ -195,7 +201,7 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
   a.out = out; a.lse = lse;
   if (scratch != nullptr) a.scratch = *scratch;
   a.build_scratch = scratch != nullptr;
-  a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
+  a.unit_rows = p.unit_rows; a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
   a.smax = p.smax;
   const int c0 = st->n_levels > 0 ? st->lvl[0].C : 1;
   a.ws_o = (float*)workspace;
