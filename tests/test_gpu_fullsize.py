@@ -1,8 +1,8 @@
 """The throughput workload at full size (B=64, D=8, 64/8 heads, d=128, bf16, 32768-token
-prefix compressed to 8192 C4 + 256 C128 entries), in the launch configuration the
-benchmark times: acceptance bit-exact for every sequence; attention, scratch and the
-refreshed state compared with the oracle on sampled sequences; counts and finiteness
-checked for all."""
+prefix compressed to 8192 C4 + 256 C128 entries), and the same batch with a 16-node tree,
+in the launch configuration the benchmark times: acceptance bit-exact for every
+sequence; attention, scratch and the refreshed state compared with the oracle on sampled
+sequences; counts and finiteness checked for all."""
 import sys
 
 import numpy as np
@@ -23,10 +23,13 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def test_high_batch_full_size():
+@pytest.mark.parametrize("name", ["high_batch", "wide_tree"])
+def test_full_size(name):
+    """high_batch: 64 query rows per KV head (4-wave units); wide_tree: D = 16, 128 rows
+    per KV head (8-wave units)."""
     import torch
-    w = synth.WORKLOADS["high_batch"]
-    _say("full size: building state")
+    w = synth.WORKLOADS[name]
+    _say(f"full size {name}: building state")
     caps = pooled_caps(w, 64)
     dst = device_state(w, caps, poison=True)
     ost = oracle_state(w, caps, batch=SAMPLE)
@@ -56,7 +59,7 @@ def test_high_batch_full_size():
     assert np.isfinite(out).all() and torch.isfinite(r.lse).all()
 
     # sampled sequences against the oracle
-    _say("full size: oracle on sampled sequences")
+    _say(f"full size {name}: oracle on sampled sequences")
     ss = synth.step_inputs(w, 0, batch=SAMPLE)
     h = widen_step(ss, w.dtype)
     ref = oracle.step(ost, ss.parents, ss.draft, ss.target, h.q, h.kt, h.vt)
