@@ -113,60 +113,85 @@ def calibrate_copy(mib: int):
     print(json.dumps({"calibrate_copy_bytes": n * 4, "launches": 5}), flush=True)
 
 
-PROFILE_BENCH = "python3 bench.py --steps 20 --warmup 40 --no-cpu-baseline --no-extras"
-PROFILE_COUNTER_BENCH = "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras"
+PROFILE_BENCH = "python3 bench.py --gpus 1 --steps 20 --warmup 5"  # the headline command itself
+PROFILE_COUNTER_BENCH = "python3 bench.py --gpus 1 --steps 20 --warmup 5 --no-cpu-baseline --no-extras"
 PREFIX_KERNEL = "tv::k_attn_mfma<4, 1, false>"  # the contiguous-pool instance the benchmark runs
+STEP_KERNELS = ("k_tree_mask", "k_scratch", "k_attn_mfma", "k_attn_finish", "k_accept", "k_refresh")
+CALL_KERNELS = ("k_scratch", "k_attn_mfma", "k_attn_finish")  # what one tv_verify_attn call launches
 
 
-def _counter_per_kernel(path: str, counter: str) -> dict:
-    """Mean value of a counter per dispatch (FETCH_SIZE / WRITE_SIZE: KiB; the derived
-    utilisation metrics: percent or a ratio), by kernel name, from a rocprofv3 csv."""
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "")
+
+
+def _headline_steps(trace_csv: str, n_steps: int) -> list:
+    """The first n_steps steps of the run from a rocprofv3 kernel trace: the library's
+    dispatches in start order, cut at each k_tree_mask (a step's first kernel); each step is
+    a list of (kernel, start ns, end ns)."""
     import csv
-    acc = {}
-    with open(path) as fh:
-        for r in csv.DictReader(fh):
-            if r["Counter_Name"] != counter:
-                continue
-            v = acc.setdefault(r["Kernel_Name"], [0.0, 0])
-            v[0] += float(r["Counter_Value"])
-            v[1] += 1
-    return {k: v[0] / v[1] for k, v in acc.items()}
+    rows = sorted(((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+                   for r in csv.DictReader(open(trace_csv)) if "tv::" in r["Kernel_Name"]), key=lambda x: x[1])
+    steps, cur = [], None
+    for k, a_, b_ in rows:
+        if "k_tree_mask" in k:
+            if cur is not None:
+                steps.append(cur)
+                if len(steps) == n_steps:
+                    return steps
+            cur = []
+        if cur is not None:
+            cur.append((k, a_, b_))
+    if cur is not None and len(steps) < n_steps:
+        steps.append(cur)
+    return steps
 
 
 def summarize_profiles(d: str, workload: str) -> None:
     """Turn the rocprofv3 csv runs of the profiling commands below into the committed
-    summaries: the kernel-trace statistics, the scaled HBM bytes per dispatch and the
-    traffic record bench.py reports (tagged with the prefix kernel's source digest)."""
+    summaries: every launch of the headline's steps in order (warm-up and timed), the
+    tv_verify_attn call's span per step and the HBM fraction that follows from the trace,
+    the scaled HBM bytes per call and the traffic record bench.py reports (tagged with the
+    digest of the call's kernel sources)."""
     import csv
     out_dir = os.path.join(ROOT, "profiles")
     bench_line = [l for l in open(os.path.join(d, "kt.txt")).read().splitlines() if l.startswith("{")][-1]
     bl = json.loads(bench_line)
+    W, K = bl["warmup"], bl["steps"]
     kt_cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {PROFILE_BENCH}"
-    rows = list(csv.DictReader(open(os.path.join(d, "kt", "run_kernel_stats.csv"))))
-    ours = [r for r in rows if "tv::" in r["Name"]]
-    total_ns = sum(float(r["TotalDurationNs"]) for r in rows)
-    lines = [f"# Kernel-trace summary: the verify step at {workload} "
-             f"(B={bl['config']['B']}, D={bl['config']['D']}, {bl['config']['Hq']}/{bl['config']['Hkv']} heads, "
-             f"d={bl['config']['head_dim']}, {bl['dtype']}, {bl['config']['prefix_tokens']}-token prefix)", "",
+    steps = _headline_steps(os.path.join(d, "kt", "run_kernel_trace.csv"), W + K)
+    alg = bl["roofline"]["algorithmic_bytes_per_launch"]
+    cfg = bl["config"]
+    lines = [f"# Kernel trace of the headline command: the verify step at {workload} "
+             f"(B={cfg['B']}, D={cfg['D']}, {cfg['Hq']}/{cfg['Hkv']} heads, d={cfg['head_dim']}, {bl['dtype']}, "
+             f"{cfg['prefix_tokens']}-token prefix)", "",
              "Command (from the repository root, TMPDIR=/tmp):", "", "    " + kt_cmd, "",
-             "Per-kernel statistics (`run_kernel_stats.csv`; calls = warm-up + timed steps).  The bench line of",
-             f"the same run reports the prefix kernel at avg {bl['roofline']['avg_launch_ms'] * 1e3:.1f} us from HIP "
-             f"events on its stream ({bl['roofline']['achieved']:.1f} GB/s).  The profiler slows the kernel; a run",
-             "of the same command without it (`python bench.py`) is the throughput figure.", "",
-             "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
-    for r in ours:
-        lines.append(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
-                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
-                     f"{100.0 * float(r['TotalDurationNs']) / total_ns:.1f}% |")
-    # the timed launches alone (the last `steps` of the prefix kernel), beside the events
-    tr = sorted((r for r in csv.DictReader(open(os.path.join(d, "kt", "run_kernel_trace.csv")))
-                 if PREFIX_KERNEL in r["Kernel_Name"]), key=lambda r: int(r["Start_Timestamp"]))
-    timed = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr[-bl["steps"]:]]
-    lines += ["", f"The {len(timed)} timed launches of `{PREFIX_KERNEL}` alone (`run_kernel_trace.csv`): average "
-              f"{sum(timed) / len(timed):.1f} us, against {bl['roofline']['avg_launch_ms'] * 1e3:.1f} us from the HIP "
-              "events of the same launches (the events also hold the dispatch of the kernel).",
-              "", "Bench line of the profiled run:", "", "    " + bench_line, ""]
-    open(os.path.join(out_dir, f"attn_prefix_{workload}_kernel_trace.md"), "w").write("\n".join(lines))
+             f"Every launch of the headline's {W} untimed and {K} timed steps, in order (`run_kernel_trace.csv`), in us.",
+             "`call` is the tv_verify_attn call on the GPU: from the start of its first kernel to the end of its last;",
+             "`step` from the step's first kernel start to its last kernel end.", "",
+             "| step | " + " | ".join(k.replace("k_", "") for k in STEP_KERNELS) + " | call | step |",
+             "|---|" + "---|" * (len(STEP_KERNELS) + 2)]
+    calls = []
+    for i, st in enumerate(steps):
+        dur = {k: 0.0 for k in STEP_KERNELS}
+        for name, a_, b_ in st:
+            for k in STEP_KERNELS:
+                if k + "<" in name or k + "(" in name:
+                    dur[k] += (b_ - a_) / 1e3
+        vk = [(a_, b_) for name, a_, b_ in st if any(k + "<" in name or k + "(" in name for k in CALL_KERNELS)]
+        call = (max(b_ for _, b_ in vk) - min(a_ for a_, _ in vk)) / 1e3 if vk else 0.0
+        span = (max(b_ for _, _, b_ in st) - min(a_ for _, a_, _ in st)) / 1e3
+        if i >= W:
+            calls.append(call)
+        lines.append(f"| {i}{'' if i >= W else ' (warm-up)'} | " + " | ".join(f"{dur[k]:.1f}" if dur[k] else "-"
+                                                                          for k in STEP_KERNELS)
+                     + f" | {call:.1f} | {span:.1f} |")
+    mean_call = sum(calls) / max(len(calls), 1)
+    lines += ["", f"Timed steps: mean call {mean_call:.1f} us in the trace; {alg / 1e9:.4f} GB algorithmic per call "
+              f"-> {alg / (mean_call * 1e-6) / 1e9:.1f} GB/s = {alg / (mean_call * 1e-6) / 1e9 / PEAK_HBM_GBS:.4f} of "
+              f"8 TB/s.  The bench line of the same run (HIP events around each call, the profiler attached): "
+              f"{bl['roofline']['avg_call_ms'] * 1e3:.1f} us, frac {bl['roofline']['frac']}.", "",
+              "Bench line of the profiled run:", "", "    " + bench_line, ""]
+    open(os.path.join(out_dir, f"verify_call_{workload}_kernel_trace.md"), "w").write("\n".join(lines))
 
     fetch = _counter_per_kernel(os.path.join(d, "FETCH_SIZE", "run_counter_collection.csv"), "FETCH_SIZE")
     write = _counter_per_kernel(os.path.join(d, "WRITE_SIZE", "run_counter_collection.csv"), "WRITE_SIZE")
@@ -177,26 +202,27 @@ def summarize_profiles(d: str, workload: str) -> None:
                                  if l.startswith("{")][-1])["calibrate_copy_bytes"])
     fs = copy_bytes / 1024.0 / cf[copy_name]
     ws = copy_bytes / 1024.0 / cw[copy_name]
-    pk = [k for k in fetch if PREFIX_KERNEL in k][0]
-    rd = fetch[pk] * 1024.0 * fs
-    wr = write[pk] * 1024.0 * ws
-    # algorithmic bytes of the counter runs themselves (their pools are at their own step)
+    in_call = [k for k in fetch if any(c + "<" in k or c + "(" in k for c in CALL_KERNELS)]
+    rd = sum(fetch[k] for k in in_call) * 1024.0 * fs
+    wr = sum(write.get(k, 0.0) for k in in_call) * 1024.0 * ws
+    # algorithmic bytes of the counter runs themselves
     fl = json.loads([l for l in open(os.path.join(d, "FETCH_SIZE.txt")).read().splitlines() if l.startswith("{")][-1])
-    alg = fl["roofline"]["algorithmic_bytes_per_launch"]
+    alg_c = fl["roofline"]["algorithmic_bytes_per_launch"]
     cmd = f"rocprofv3 --pmc {{}} --output-format csv -d <dir> -o run -- {PROFILE_COUNTER_BENCH}"
-    rec = {"kernel": pk, "workload": workload,
+    rec = {"kernels": [_short(k) for k in in_call], "workload": workload,
            "command_fetch": cmd.format("FETCH_SIZE"), "command_write": cmd.format("WRITE_SIZE"),
            "command_calibration": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d <dir> -o run -- "
                                   "python3 bench.py --calibrate-copy 1024",
-           "fetch_size_kib_per_dispatch": round(fetch[pk], 2), "write_size_kib_per_dispatch": round(write[pk], 2),
+           "fetch_size_kib_per_call": round(sum(fetch[k] for k in in_call), 2),
+           "write_size_kib_per_call": round(sum(write.get(k, 0.0) for k in in_call), 2),
            "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_size_kib": round(cf[copy_name], 2),
                                 "write_size_kib": round(cw[copy_name], 2), "fetch_scale": round(fs, 5),
                                 "write_scale": round(ws, 5)},
            "hbm_bytes_per_launch": int(rd + wr), "hbm_read_bytes_per_launch": int(rd),
-           "hbm_write_bytes_per_launch": int(wr), "algorithmic_bytes_per_launch": alg,
-           "hbm_over_algorithmic": round((rd + wr) / alg, 4), "kernel_source_digest": kernel_source_digest()}
-    open(os.path.join(out_dir, f"traffic_attn_prefix_{workload}.json"), "w").write(json.dumps(rec, indent=1) + "\n")
-    lines = [f"# HBM bytes per dispatch (FETCH_SIZE, WRITE_SIZE): the verify step at {workload}", "",
+           "hbm_write_bytes_per_launch": int(wr), "algorithmic_bytes_per_launch": alg_c,
+           "hbm_over_algorithmic": round((rd + wr) / alg_c, 4), "kernel_source_digest": kernel_source_digest()}
+    open(os.path.join(out_dir, f"traffic_verify_call_{workload}.json"), "w").write(json.dumps(rec, indent=1) + "\n")
+    lines = [f"# HBM bytes per tv_verify_attn call (FETCH_SIZE, WRITE_SIZE): the verify step at {workload}", "",
              "Commands (from the repository root, TMPDIR=/tmp), one counter per run:", "",
              "    " + cmd.format("FETCH_SIZE"), "    " + cmd.format("WRITE_SIZE"),
              "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python3 bench.py --calibrate-copy 1024",
@@ -208,10 +234,11 @@ def summarize_profiles(d: str, workload: str) -> None:
     for k in sorted(fetch):
         if "tv::" not in k:
             continue
-        lines.append(f"| `{k.split('(')[0].replace('void ', '')}` | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | "
+        lines.append(f"| `{_short(k)}` | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | "
                      f"{fetch[k] * 1024 * fs / 1e6:.2f} | {write.get(k, 0.0) * 1024 * ws / 1e6:.2f} |")
-    lines += ["", f"Prefix kernel: {(rd + wr) / 1e9:.4f} GB of HBM traffic per launch against {alg / 1e9:.4f} GB "
-              f"algorithmic: ratio {(rd + wr) / alg:.4f}.", ""]
+    lines += ["", f"The tv_verify_attn call ({', '.join('`' + _short(k) + '`' for k in in_call)}): "
+              f"{(rd + wr) / 1e9:.4f} GB of HBM traffic per call against {alg_c / 1e9:.4f} GB algorithmic: "
+              f"ratio {(rd + wr) / alg_c:.4f}.", ""]
     open(os.path.join(out_dir, f"hbm_bytes_{workload}.md"), "w").write("\n".join(lines))
     util = os.path.join(d, "util", "run_counter_collection.csv")
     if os.path.exists(util):
@@ -243,7 +270,7 @@ def summarize_utilisation(path: str, workload: str, bench_line: dict) -> None:
         bench_line["config"]["head_dim"] * bench_line["roofline"]["algorithmic_bytes_per_launch"] / \
         (bench_line["config"]["B"] * bench_line["config"]["Hkv"] * bench_line["config"]["head_dim"] * 4.0)
     lines += ["", f"Algorithmic MFMA work of the prefix kernel at this shape: about {flops / 1e12:.3f} TFLOP per launch "
-              f"(4 * B * Hq * D * d per committed entry), {flops / (bench_line['roofline']['avg_launch_ms'] * 1e-3) / 1e12:.0f} "
+              f"(4 * B * Hq * D * d per committed entry), {flops / (bench_line['roofline']['avg_call_ms'] * 1e-3) / 1e12:.0f} "
               "TFLOP/s at the launch time of the same run, against 2500 TFLOP/s dense bf16: the kernel is bound by HBM, "
               "and the matrix cores are busy for the share of cycles shown.", ""]
     open(os.path.join(ROOT, "profiles", f"utilisation_{workload}.md"), "w").write("\n".join(lines))
@@ -273,7 +300,7 @@ def summarize_step_trace(d: str, workload: str) -> None:
              f"Per-kernel statistics over every step of the run (untimed settling steps, then the timed ones: {calls} "
              "launches of each kernel).  The profiler adds its own overhead per launch;",
              f"the bench line of the same run: {line['ms_per_step'] * 1e3:.1f} us per step, verify launch "
-             f"{line['roofline']['avg_launch_ms'] * 1e3:.1f} us (HIP events).", "",
+             f"{line['roofline']['avg_call_ms'] * 1e3:.1f} us (HIP events).", "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in rows:
         lines.append(f"| `{r['Name'].split('(')[0].replace('void ', '')}` | {r['Calls']} | "
@@ -308,17 +335,19 @@ def summarize_sweep_traces(d: str) -> None:
 
 
 def kernel_source_digest() -> str:
+    """Digest of the sources of every kernel a tv_verify_attn call can launch and of the
+    host code that plans it."""
     h = hashlib.sha256()
-    for f in ("attn_mfma.hip", "scratch_pad.h", "tv_common.h"):
+    for f in ("attn_mfma.hip", "scratch_pad.h", "scratch.hip", "attn_merge.hip", "tv_common.h", "tv_host.cpp"):
         with open(os.path.join(ROOT, "tree_speculative_decoding_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the prefix kernel from committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_attn_prefix_{workload}.json")
+    """HBM bytes per tv_verify_attn call from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_verify_call_{workload}.json")
     if not os.path.exists(p):
         return None
     with open(p) as fh:
@@ -382,12 +411,18 @@ class StepRunner:
                     q=tv.to_device(s.q, self.w.dtype), kt=tv.to_device(s.k_tree, self.w.dtype),
                     vt=tv.to_device(s.v_tree, self.w.dtype))
 
-    def step(self, st, x: dict):
+    def step(self, st, x: dict, attn_ev=None):
+        """One step; attn_ev = (start, stop) events recorded on the stream around the whole
+        tv_verify_attn call (every kernel it launches)."""
         import tree_speculative_decoding_amd as tv
         s = self.stream
         tv.tv_build_tree_mask(x["parents"], self.anc, self.depth, self.err, s)
+        if attn_ev is not None:
+            record(attn_ev[0], s)
         tv.tv_verify_attn(x["q"], x["kt"], x["vt"], self.anc, self.depth, self.err, st, self.sc, self.out, self.lse,
                           self.ws, self.parts, s)
+        if attn_ev is not None:
+            record(attn_ev[1], s)
         if self.fused:
             tv.tv_accept_refresh(st, self.sc, x["parents"], self.anc, self.depth, x["draft"], x["target"], x["kt"],
                                  x["vt"], self.m, self.path, self.bonus, self.log, self.err, s)
@@ -421,9 +456,9 @@ def settle_warmup(runner: StepRunner, states: list, sets: list, warmup: int, set
 def timed_steps(runner: StepRunner, states: list, sets: list, warmup: int, steps: int) -> dict:
     """`warmup` untimed steps, then `steps` timed ones, rotating over `states` (so that a
     small working set is read cold from HBM each step) and the input `sets`.  Returns the
-    whole region's time, per-step times (fence-free events between steps), the attention
-    kernel's per-launch times (events the library records around it) and the committed
-    lengths before and after the timed steps."""
+    whole region's time, per-step times (fence-free events between steps), the times of
+    the tv_verify_attn calls (fence-free events on the stream around each call: every
+    kernel the call launches) and the committed lengths before and after the timed steps."""
     import torch
     import tree_speculative_decoding_amd as tv
     stream = runner.stream
@@ -439,11 +474,9 @@ def timed_steps(runner: StepRunner, states: list, sets: list, warmup: int, steps
     start.record(stream)
     for t in range(steps):
         record(step_ev[t], stream)
-        tv.tv_set_timing_events(attn_ev[t][0], attn_ev[t][1])
-        runner.step(states[(warmup + t) % len(states)], sets[(warmup + t) % len(sets)])
+        runner.step(states[(warmup + t) % len(states)], sets[(warmup + t) % len(sets)], attn_ev[t])
     record(step_ev[steps], stream)
     stop.record(stream)
-    tv.tv_set_timing_events(None, None)
     torch.cuda.synchronize()
     n_before = [sum(int(x.sum()) for x in nd) for nd in n_dev]
     return {"total_ms": start.elapsed_time(stop),
@@ -555,7 +588,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "k_attn_mfma (prefix stream + tail + chain)", "avg_launch_ms": round(attn_avg_ms, 5),
+                     "kernel": "tv_verify_attn call (scratch pad, prefix stream with tail and chain, merge if any)",
+                     "avg_call_ms": round(attn_avg_ms, 5),
                      "algorithmic_bytes_per_launch": int(attn_bytes)},
         "step_ms_p10_p50_p90": [round(pct(r["step_ms"], q), 4) for q in (10, 50, 90)],
         **({"warm": warm} if n_rot > 1 else {}),
@@ -566,22 +600,17 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     if not args.no_extras:
-        # the same timed steps from the same starting state, captured in one HIP graph
-        graph_ms = graph_step_ms(runner, states, sets, args.steps, states, saved_all)
-        result["graph_ms_per_step"] = round(graph_ms, 4)
-        result["graph_tokens_per_s"] = round(B * D / (graph_ms * 1e-3), 1)
-        # the same steps with acceptance and refresh fused into one launch
-        for x, sv in zip(states, saved_all):
-            restore(x, sv)
-        runner.fused = True
-        rf = timed_steps(runner, states, sets, args.warmup, args.steps)
-        fused_graph_ms = graph_step_ms(runner, states, sets, args.steps, states, saved_all)
-        runner.fused = False
+        # the same steps with acceptance and refresh fused, and both step forms replayed from
+        # captured graphs: alternating blocks from the same starting state (A/B in one run)
+        ab = ab_blocks(runner, states, sets, args.steps, args.warmup, saved_all)
+        result["graph_ms_per_step"] = ab["graph"]
+        result["graph_tokens_per_s"] = round(B * D / (ab["graph"] * 1e-3), 1)
         result["fused_accept_refresh"] = {
-            "ms_per_step": round(rf["total_ms"] / args.steps, 4),
-            "graph_ms_per_step": round(fused_graph_ms, 4),
-            "graph_tokens_per_s": round(B * D / (fused_graph_ms * 1e-3), 1),
-            "note": "tv_accept_refresh in place of tv_accept + tv_refresh_state; same steps, same starting state"}
+            "ms_per_step": ab["eager_fused"], "graph_ms_per_step": ab["graph_fused"],
+            "graph_tokens_per_s": round(B * D / (ab["graph_fused"] * 1e-3), 1),
+            "same_blocks_eager_ms_per_step": ab["eager"],
+            "note": "tv_accept_refresh in place of tv_accept + tv_refresh_state; medians of alternating blocks "
+                    "(eager, eager fused, graph, graph fused; rotated order) from the same starting state"}
         ceiling = read_ceiling(stream)
         ceiling["attn_frac_of_ceiling"] = round(achieved / ceiling["GB/s"], 4)
         result["read_ceiling"] = ceiling
@@ -722,7 +751,6 @@ def graph_step_ms(runner: StepRunner, sts: list, sets: list, steps: int, states:
         torch.cuda.synchronize()
 
     reset()
-    tv.tv_set_timing_events(None, None)
     g = torch.cuda.CUDAGraph()
     eager_stream = runner.stream
     with torch.cuda.graph(g):
@@ -742,6 +770,69 @@ def graph_step_ms(runner: StepRunner, sts: list, sets: list, steps: int, states:
     ms = start.elapsed_time(stop) / steps
     del g
     return ms
+
+
+AB_ROUNDS = 3
+
+
+def ab_blocks(runner: StepRunner, states: list, sets: list, steps: int, warmup: int, saved: list) -> dict:
+    """The four step forms -- eager four calls, eager with tv_accept_refresh, and both
+    replayed from a captured HIP graph -- timed in AB_ROUNDS rounds of alternating blocks,
+    each block from the same restored starting state (`warmup` untimed steps or one untimed
+    replay first), the order rotated every round, all queued without a host
+    synchronisation.  Returns the median ms per step of each form."""
+    import torch
+
+    def reset():
+        for st, sv in zip(states, saved):
+            restore(st, sv)
+
+    graphs = {}
+    for name, fused in (("graph", False), ("graph_fused", True)):
+        reset()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        eager_stream = runner.stream
+        runner.fused = fused
+        with torch.cuda.graph(g):
+            runner.stream = torch.cuda.current_stream()
+            for t in range(steps):
+                runner.step(states[t % len(states)], sets[t % len(sets)])
+        runner.stream = eager_stream
+        graphs[name] = g
+    runner.fused = False
+    stream = runner.stream
+    forms = ["eager", "eager_fused", "graph", "graph_fused"]
+    ev = {f: [] for f in forms}
+    reset()
+    torch.cuda.synchronize()
+    for r in range(AB_ROUNDS):
+        for f in forms[r % 4:] + forms[:r % 4]:
+            a_, b_ = TimingEvent(), TimingEvent()
+            reset()
+            if f.startswith("graph"):
+                graphs[f].replay()
+                reset()
+                record(a_, stream)
+                graphs[f].replay()
+                record(b_, stream)
+            else:
+                runner.fused = f == "eager_fused"
+                for t in range(warmup):
+                    runner.step(states[t % len(states)], sets[t % len(sets)])
+                reset()
+                record(a_, stream)
+                for t in range(steps):
+                    runner.step(states[t % len(states)], sets[t % len(sets)])
+                record(b_, stream)
+                runner.fused = False
+            ev[f].append((a_, b_))
+    torch.cuda.synchronize()
+    out = {f: round(float(np.median([a_.elapsed_ms(b_) / steps for a_, b_ in ev[f]])), 4) for f in forms}
+    del graphs
+    reset()
+    torch.cuda.synchronize()
+    return out
 
 
 def snapshot(st) -> dict:
@@ -769,8 +860,9 @@ def write_sweep_table(args, rows: list, ceiling: dict) -> None:
            f"({100 * ceiling['frac_of_peak']:.1f}% of 8 TB/s).  `cold`: states rotated so each step reads "
            "its pools from HBM; `warm`: one state back to back (batch 1 and 4 fit the 256 MB last-level "
            "cache partly or wholly); `hbm`: one state larger than 1 GiB.  Every point first runs untimed "
-           "steps for at least 15 ms.  Attention = the prefix-stream kernel per launch (mean over the timed "
-           "steps, p10 / p90 beside it; the merge kernel of split units is in the step time); intensity = "
+           "steps for at least 15 ms.  Attention = the tv_verify_attn call (every kernel it launches: the "
+           "scratch pad when it runs apart, the prefix stream, the merge of split prefixes), mean over the timed "
+           "steps, p10 / p90 beside it; intensity = "
            "attention flops per algorithmic byte; graph = the same steps replayed from one captured HIP "
            "graph; graph fused = the same with tv_accept_refresh in place of tv_accept + tv_refresh_state.", "",
            "| D | B | top-k | p | mode | intensity | attn us (p10-p90) | attn GB/s | % of 8 TB/s | % of ceiling "
@@ -860,9 +952,9 @@ def time_draft_attn(w, st, stream, reps: int) -> dict:
             tv.tv_draft_attn(qd, kd, vd, anc, err, st, out, None, ws, stream=stream)
         ev = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
         for a_, b_ in ev:
-            tv.tv_set_timing_events(a_, b_)
+            record(a_, stream)
             tv.tv_draft_attn(qd, kd, vd, anc, err, st, out, None, ws, stream=stream)
-        tv.tv_set_timing_events(None, None)
+            record(b_, stream)
         torch.cuda.synchronize()
         ms = float(np.mean([a_.elapsed_ms(b_) for a_, b_ in ev]))
         nbytes = w.B * (w.Hkv * (entries + tail) * w.d * 2 * e + D * w.Hq * w.d * 2 * e + D * w.Hkv * w.d * 2 * e
@@ -915,10 +1007,10 @@ def time_paged(w, st, stream, reps: int) -> dict:
         for which, state in ((0, st), (1, sp)):
             for _ in range(reps):
                 a_, b_ = TimingEvent(), TimingEvent()
-                tv.tv_set_timing_events(a_, b_)
+                record(a_, stream)
                 tv.tv_verify_attn(q, kt, vt, anc, depth, err, state, None, out[which], None, ws, 0, stream)
+                record(b_, stream)
                 ev[which].append((a_, b_))
-    tv.tv_set_timing_events(None, None)
     torch.cuda.synchronize()
     ms = {k: [a_.elapsed_ms(b_) for a_, b_ in v] for k, v in ev.items()}
     same = bool(torch.equal(out[0].view(torch.int16), out[1].view(torch.int16))) if w.dtype == "bf16" else \

@@ -58,7 +58,7 @@ extern "C" {
 #define TV_API
 #endif
 
-#define TV_VERSION 120      /* 1.2.0: contiguous pools in runs of TV_TILE_RUN tiles */
+#define TV_VERSION 130      /* 1.3.0: workspace holds only the partials of split prefixes */
 #define TV_MAX_LEVELS 2
 #define TV_MAX_D 64
 #define TV_TILE_RUN 16     /* tiles of one (sequence, KV head) kept together in a contiguous pool */
@@ -178,9 +178,12 @@ TV_API tv_status tv_build_draft_tree(int B, int topk, int steps, int D, int voca
  * shared-prefix stream is cut into num_parts equal slices, one workgroup each
  * (0 = the library's choice for the current device: one full round of resident
  * workgroups; the same value must then be passed to tv_verify_attn).  The slices run
- * over every (sequence, KV head, 64-query-row block) prefix laid end to end, so any
- * batch size keeps the whole GPU busy; each slice leaves one partial (max, sum,
- * unnormalised output) per prefix it touches.  Returns 0 on invalid arguments.
+ * over every (sequence, KV head, block of query rows) prefix laid end to end, so any
+ * batch size keeps the whole GPU busy; a prefix split over several slices gets one
+ * partial (max, sum, unnormalised output) per slice, merged after the stream.  When no
+ * prefix is split (e.g. 64 sequences of 8 KV heads on 256 compute units) nothing is
+ * written to the workspace and 256 bytes are asked for.  The contents need no
+ * initialisation and are dead after the call.  Returns 0 on invalid arguments.
  */
 TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, int num_parts);
 
@@ -291,11 +294,6 @@ TV_API tv_status tv_accept_refresh(int D, const tv_state* st, const tv_scratch* 
  */
 TV_API tv_status tv_compress_prefix(const tv_state* st, const void* raw_k, const void* raw_v,
                                     int max_len, int32_t* seq_err, hipStream_t stream);
-
-/* Optional timing hook: when both events are non-NULL, later tv_verify_attn calls
- * on this host thread record `start` just before and `stop` just after the
- * prefix-streaming attention kernel, on the call's stream.  NULL, NULL turns it off. */
-TV_API tv_status tv_set_timing_events(hipEvent_t start, hipEvent_t stop);
 
 TV_API const char* tv_status_string(tv_status s);
 TV_API const char* tv_last_error(void);   /* this thread's last argument/launch error */

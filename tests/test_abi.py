@@ -15,7 +15,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert tv.tv_version() == 120
+    assert tv.tv_version() == 130
 
 
 def test_struct_layout_matches_header():
@@ -90,8 +90,15 @@ def test_verify_rejects_bad_levels_and_workspace():
     assert L.tv_verify_attn(8, 15, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, 1 << 30, 1, None) == tv.TV_EINVAL  # Hq % Hkv
     need = L.tv_verify_attn_workspace_bytes(8, 16, ctypes.byref(s), 3)
     # 4 units (2 seq x 2 heads x 1 row block) of 2 + 2 chunks = 16 chunks in 3 slices of 6:
-    # a prefix meets at most 2 slices -> 2 partial slots of 64 rows x (128 + 2) floats
-    assert need == 2 * 2 * 2 * 64 * 128 * 4 + 2 * 2 * 2 * 64 * 8
+    # (slice, unit) pairs are numbered slice + unit < 3 + 4 - 1 -> 6 partial blocks of 64
+    # rows x (128 floats + a (max, sum) pair)
+    assert need == 6 * 64 * 128 * 4 + 6 * 64 * 8
+    # 4 slices of 4 chunks: every prefix is one slice's, nothing goes to the workspace
+    assert L.tv_verify_attn_workspace_bytes(8, 16, ctypes.byref(s), 4) == 256
+    # the fp32 vector kernel always writes partials (its merge adds the tail and the chain)
+    s.dtype = 0
+    assert L.tv_verify_attn_workspace_bytes(8, 16, ctypes.byref(s), 4) == (4 + 4 - 1) * 64 * (128 * 4 + 8)
+    s.dtype = 1
     assert L.tv_verify_attn(8, 16, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, need - 1, 3, None) == tv.TV_EWORKSPACE
     assert L.tv_verify_attn_workspace_bytes(0, 16, ctypes.byref(s), 3) == 0
 
@@ -104,7 +111,6 @@ def test_refresh_and_compress_reject_bad_args():
     assert L.tv_refresh_state(8, ctypes.byref(s), ctypes.byref(sc), P, P, P, P, None, P, None) == tv.TV_EINVAL
     assert L.tv_compress_prefix(ctypes.byref(s), P, P, -1, P, None) == tv.TV_EINVAL
     assert L.tv_compress_prefix(ctypes.byref(s), None, P, 10, P, None) == tv.TV_EINVAL
-    assert L.tv_set_timing_events(P, None) == tv.TV_EINVAL
 
 
 def test_accept_refresh_rejects_bad_args():

@@ -105,12 +105,41 @@ def test_verify_tree_dominant():
     assert np.abs(wrong - res["out"]).max() > 10 * ATT_ATOL["bf16"]
 
 
-@pytest.mark.parametrize("parts", [1, 2, 3, 7, 33, 1000])
-def test_partition_invariance(parts):
+# 12 nodes x 8 query heads per KV head = 96 rows: 128-row units in 8-wave workgroups
+WIDE_SMALL = synth.Workload("wide_small", 3, 12, 64, 8, 128, "bf16", (4, 128), 4099, 2, 4, 0.6, 1501, prefix="raw")
+
+
+@pytest.mark.parametrize("name,parts", [("linear", p) for p in (1, 2, 3, 7, 33, 1000)] +
+                         [("wide_small", p) for p in (1, 3, 33, 1000)])
+def test_partition_invariance(name, parts):
     """Any cut of the prefix stream into workgroup slices gives the same result (within
-    tolerance): slices that start or end inside a prefix, several prefixes per slice."""
-    _say(f"verify parts={parts}")
-    check_outputs(run_verify(synth.WORKLOADS["linear"], num_parts=parts))
+    tolerance): slices that start or end inside a prefix, several prefixes per slice; for
+    64-row and 128-row units.  The scratch pad is built where the cut puts it (workgroups
+    ahead of or behind the stream's in the same launch, or a kernel of its own) and
+    matches the oracle in every case."""
+    _say(f"verify {name} parts={parts}")
+    w = WIDE_SMALL if name == "wide_small" else synth.WORKLOADS[name]
+    res = run_verify(w, num_parts=parts)
+    check_outputs(res)
+    check_scratch(res)
+
+
+def test_scratch_pad_paths_bit_identical():
+    """The scratch pad built by workgroups ahead of the stream's in the prefix launch (a
+    small cut leaves room for them), behind them (a cut that fills the device) and by the
+    scratch kernel of its own (128-row units) is the same bits: the same code adds the same
+    values in the same order."""
+    _say("scratch pad paths")
+    import torch
+    w = synth.WORKLOADS["linear"]
+    a = run_verify(w, num_parts=64)     # 64 stream + 64 pad workgroups fit: pad ahead of the stream
+    b = run_verify(w, num_parts=1000)   # no room: pad workgroups behind the stream's
+    for l in range(len(w.levels)):
+        for name in ("entry_k", "entry_v", "open_k", "open_v"):
+            x, y = getattr(a["r"].sc, name)[l], getattr(b["r"].sc, name)[l]
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)), (l, name)
+    check_scratch(a)
 
 
 def test_determinism_bit_identical():

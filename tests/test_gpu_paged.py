@@ -34,6 +34,9 @@ VERIFY = {
     "tree_bf16_split": (synth.WORKLOADS["tree"], 7),        # units split over slices: merge kernel
     "bf16_ragged": (synth.Workload("pg1", 3, 5, 40, 8, 128, "bf16", (4, 128), 4733, 2, 3, 0.6, 4001, prefix="raw"), 0),
     "f32_d64": (synth.Workload("pg2", 2, 8, 8, 2, 64, "f32", (4, 16), 603, 2, 3, 0.6, 4002, prefix="raw"), 0),
+    # 96 query rows per KV head (128-row units, 8 waves) with tail + tree = 3 + 12 <= 16 entries
+    "bf16_wide_tt1": (synth.Workload("pg3", 2, 12, 64, 8, 128, "bf16", (4, 128), 4099, 2, 4, 0.6, 4003,
+                                     prefix="raw"), 0),
 }
 
 

@@ -144,6 +144,58 @@ def test_pool_full_leaves_sequence_unchanged():
         assert torch.equal(dst.tail_k[b], before[4][b])
 
 
+def test_bad_path_leaves_state_unchanged():
+    """tv_refresh_state with an accepted length m >= D, or a path node outside 0..D-1,
+    flags the sequence TV_SEQ_BAD_PATH and leaves its state bit-identical; the other
+    sequences of the batch are refreshed as usual (against the oracle)."""
+    import torch
+    import tree_speculative_decoding_amd as tv
+    _say("refresh bad path")
+    w = synth.Workload("badpath", 4, 8, 16, 2, 128, "bf16", (4, 128), 125, 2, 3, 0.8, 3210, prefix="raw")
+    caps = pooled_caps(w, 64)
+    dst = device_state(w, caps)
+    ost = oracle_state(w, caps)
+    r = Runner(dst, w.D, w.Hq)
+    s = synth.step_inputs(w, 0)
+    h = widen_step(s, w.dtype)
+    x = upload_step(s, w.dtype)
+    r.plan(x)
+    r.attend(x)
+    r.accept(x)
+    torch.cuda.synchronize()
+    ref = oracle.step(ost, s.parents, s.draft, s.target, h.q, h.kt, h.vt)
+    assert (r.m.cpu().numpy() == ref.m).all()
+    snap = lambda: [t.clone() for t in (dst.P, *dst.n, *dst.open_k, *dst.open_v, dst.tail_k, dst.tail_v,
+                                         *(dst.logical_k(l) for l in range(2)), *(dst.logical_vt(l) for l in range(2)))]
+    before = snap()
+    m = r.m.clone()
+    path = r.path.clone()
+    m[1] = w.D          # m >= D
+    path[2, 0] = w.D    # a node outside 0..D-1 (the root position)
+    path[3, 0] = -1
+    r.m.copy_(m)
+    r.path.copy_(path)
+    r.refresh(x)
+    torch.cuda.synchronize()
+    e = r.err.cpu().numpy()
+    assert e[0] == 0 and (e[1:] == tv.TV_SEQ_BAD_PATH).all(), e
+    after = snap()
+    for x0, x1 in zip(before, after):
+        v0 = x0.view(torch.int16) if x0.dtype == torch.bfloat16 else x0.view(torch.int32)
+        v1 = x1.view(torch.int16) if x1.dtype == torch.bfloat16 else x1.view(torch.int32)
+        assert torch.equal(v0[1:], v1[1:])
+    # sequence 0 was refreshed as the oracle says
+    assert dst.P[0].item() == ref.state.P[0]
+    compare_state(dst, _one_seq(ref.state, 0), w.dtype, "bad-path batch, sequence 0", batch=[0])
+
+
+def _one_seq(st: oracle.State, b: int) -> oracle.State:
+    pick = lambda a: a[b:b + 1].copy()
+    return oracle.State(st.levels, [pick(a) for a in st.pool_k], [pick(a) for a in st.pool_v],
+                        [pick(a) for a in st.n], [pick(a) for a in st.open_k], [pick(a) for a in st.open_v],
+                        pick(st.tail_k), pick(st.tail_v), pick(st.P))
+
+
 FUSED = {
     "bf16_c4_c128": (synth.Workload("fu1", 4, 8, 16, 2, 128, "bf16", (4, 128), 122, 2, 3, 0.8, 3301, prefix="raw"), 40),
     "f32_d64_c4_c16": (synth.Workload("fu2", 3, 7, 8, 2, 64, "f32", (4, 16), 13, 2, 3, 0.6, 3302, prefix="raw"), 30),

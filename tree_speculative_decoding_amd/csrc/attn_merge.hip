@@ -67,18 +67,21 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
     // partials of the shared prefix: one per workgroup whose slice touched this unit
     const long long u = (long long)bg * a.row_blocks + rb;
     const int n_parts = a.parts > 0 ? unit_part_count(u, a.tmax, a.per) : 0;
+    const long long p0 = a.parts > 0 ? unit_first_part(u, a.tmax, a.per) : 0;
     // with the tail and chain attended by the prefix kernel, a unit it covered with one
     // workgroup is already written; otherwise its partials already hold tail and chain
     if (a.fused_tree && n_parts == 1) return;
     float m = -INFINITY, l = 0.f, o[EPL];
 #pragma unroll
     for (int x = 0; x < EPL; ++x) o[x] = 0.f;
-    const size_t row0 = bg * a.smax * a.R + r;  // slice s of this row: row0 + s * R
+    // slice s of this row (workgroup p0 + s, pair p0 + s + u): row0 + s * unit_rows
+    const size_t row0 = partial_row(a, p0, u, r - rb * a.unit_rows);
+    const size_t sstride = (size_t)a.unit_rows;
     // (max, sum) of slice s0 + lane; lanes past the last slice read the last one's and
     // drop it by selection
     auto slice_ml = [&](int s0) {
       const int s = min(s0 + lane, n_parts - 1);
-      float2 ml = a.ws_ml[row0 + (size_t)s * a.R];
+      float2 ml = a.ws_ml[row0 + (size_t)s * sstride];
       asm volatile("" ::"v"(ml.x), "v"(ml.y));
       if (s0 + lane >= n_parts) ml.y = 0.f;
       return ml;
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
           for (int t = 0; t < kMergeBatch; ++t) {
             const int tt = min(t0 + t, cnt - 1);  // in range; weight 0 past cnt
             ct[t] = t0 + t < cnt ? __shfl(c, tt, 64) : 0.f;
-            const float* src = a.ws_o + (row0 + (size_t)(s0 + tt) * a.R) * DH + lane * EPL;
+            const float* src = a.ws_o + (row0 + (size_t)(s0 + tt) * sstride) * DH + lane * EPL;
 #pragma unroll
             for (int x = 0; x < EPL; ++x) v[t][x] = src[x];
           }

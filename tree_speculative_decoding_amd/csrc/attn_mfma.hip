@@ -89,12 +89,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, grp = lane >> 4;
-  if (NW == 4 && (int)blockIdx.x < a.fold_scratch) {  // a scratch-pad workgroup (uniform; 256 threads)
-    const int sb = blockIdx.x / a.D;
-    scratch_node<uint16_t, 4>(a, sb, blockIdx.x - sb * a.D, (int*)smem);  // (4: no spill beside the stream's registers)
+  // scratch-pad workgroups (uniform; 256 threads): the first fold_scratch workgroups, or,
+  // with pad_after, the last ones (dispatched as the stream's workgroups retire)
+  const int pad0 = a.pad_after ? a.parts : 0;
+  if (NW == 4 && (int)blockIdx.x >= pad0 && (int)blockIdx.x < pad0 + a.fold_scratch) {
+    const int item = blockIdx.x - pad0;
+    const int sb = item / a.D;
+    scratch_node<uint16_t, 4>(a, sb, item - sb * a.D, (int*)smem);  // (4: no spill beside the stream's registers)
     return;
   }
-  const int part = blockIdx.x - a.fold_scratch;  // this workgroup's slice of the stream
+  const int part = a.pad_after ? (int)blockIdx.x : (int)blockIdx.x - a.fold_scratch;  // this workgroup's slice
   // two chunks of loads in flight (8 waves: a third measured nothing, the LDS reads of 8
   // waves per chunk bound that instance)
   uint4 kpa[PER], vpa[PER], kpb[PER], vpb[PER];
@@ -107,7 +111,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
     const long long u = cg / a.tmax;
     const int c_first = (int)(cg - u * a.tmax);
     const int c_last = (int)min((long long)a.tmax, cend - u * a.tmax);
-    const int slot = (int)(part - unit_first_part(u, a.tmax, a.per));
     const bool whole_unit = c_first == 0 && c_last == a.tmax;  // no other workgroup touches it
     const int rb = (int)(u % a.row_blocks);
     const int g = (int)((u / a.row_blocks) % a.Hkv);
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
           if (a.lse != nullptr && grp == 0) a.lse[((size_t)b * a.D + node) * a.Hq + head] = -INFINITY;
         }
       } else {
-        const size_t wrow = ((bg * a.smax + slot) * a.R + row);
+        const size_t wrow = partial_row(a, part, u, w * 16 + n16);
         float* o = a.ws_o + wrow * kDH;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) *(f32x4*)(o + 16 * dt + 4 * grp) = oacc[dt];

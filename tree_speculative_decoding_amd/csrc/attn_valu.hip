@@ -35,7 +35,6 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
     const long long u = cg / a.tmax;
     const int c_first = (int)(cg - u * a.tmax);
     const int c_last = (int)min((long long)a.tmax, cend - u * a.tmax);
-    const int slot = (int)(blockIdx.x - unit_first_part(u, a.tmax, a.per));
     const int rb = (int)(u % a.row_blocks);
     const int g = (int)((u / a.row_blocks) % a.Hkv);
     const int b = (int)(u / ((long long)a.row_blocks * a.Hkv));
@@ -130,7 +129,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
     l_run += __shfl_xor(l_run, 1, 64);
     l_run += __shfl_xor(l_run, 2, 64);
     if (row < a.R) {
-      const size_t wr = (bg * a.smax + slot) * a.R + row;
+      const size_t wr = partial_row(a, blockIdx.x, u, r_loc);
 #pragma unroll
       for (int x = 0; x < DQ; ++x) a.ws_o[wr * DH + part * DQ + x] = o[x];
       if (part == 0) a.ws_ml[wr] = make_float2(m_run, l_run);
@@ -141,6 +140,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
 
 hipError_t launch_attn_valu(const AttnArgs& a, hipStream_t s) {
   if (a.parts == 0) return hipSuccess;
+  if (a.unit_rows != 64) return hipErrorInvalidValue;  // this kernel's units are 64 rows
   dim3 grid(a.parts), block(256);
   if (a.dtype == TV_BF16) {
     if (a.d == 128)

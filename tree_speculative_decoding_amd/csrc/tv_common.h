@@ -131,28 +131,37 @@ struct AttnArgs {
   float* lse;                        // may be null
   tv_scratch scratch;                // entries may be null
   int build_scratch;
-  // Prefix-stream partition.  A unit is one (sequence, KV head, 64-row block); its prefix
-  // is `tmax` 64-entry chunks long (a bound from the pool capacities; chunks past a
-  // sequence's committed entries are empty).  The units' chunks, laid end to end, are cut
-  // into `parts` equal slices of `per` chunks, one workgroup each; a workgroup writes one
-  // partial per unit its slice touches, in slot (workgroup - first workgroup of the unit).
+  // Prefix-stream partition.  A unit is one (sequence, KV head, block of unit_rows query
+  // rows); its prefix is `tmax` 64-entry chunks long (a bound from the pool capacities;
+  // chunks past a sequence's committed entries are empty).  The units' chunks, laid end
+  // to end, are cut into `parts` equal slices of `per` chunks, one workgroup each.  A
+  // slice touches a run of consecutive units, and consecutive slices share at most one
+  // unit, so (slice p, unit u) pairs are numbered uniquely by p + u (< parts + units - 1):
+  // the partial of that pair is the workspace's row block p + u (partial_row()).
   int unit_rows;                     // query rows of a unit: 64, or 128 for the 8-wave MFMA instance
   int row_blocks;                    // RB = ceil(R / unit_rows)
   int tmax;                          // chunks per unit
   long long units;                   // B * Hkv * RB
   int parts;                         // workgroups of the prefix stream
   long long per;                     // chunks per workgroup
-  int smax;                          // partial slots per unit
   int fused_tree;                    // the MFMA prefix kernel also attends to the raw tail and
                                      // the tree chunk, and writes whole units' rows itself
   int tree_tiles;                    // 16-entry tiles of that chunk: 1, 2 or 4
   int fold_scratch;                  // MFMA prefix kernel: its first fold_scratch workgroups
                                      // build the scratch pad (one per (sequence, node)), the
                                      // prefix stream's `parts` workgroups follow
-  float* ws_o;                       // [B][Hkv][smax][R][d]
-  float2* ws_ml;                     // [B][Hkv][smax][R] (running max in log2 units, sum)
+  int pad_after;                     // the fold_scratch workgroups come after the stream's instead
+                                     // (they then fill the slots of the first slices to finish)
+  float* ws_o;                       // [parts + units - 1][unit_rows][d] (unused if no unit is split)
+  float2* ws_ml;                     // [parts + units - 1][unit_rows] (running max in log2 units, sum)
   float scale_log2;                  // log2(e) / sqrt(d)
 };
+
+// Workspace row of the partial that slice `part` leaves for local row `lrow` (0 ..
+// unit_rows-1) of unit u.
+__device__ __forceinline__ size_t partial_row(const AttnArgs& a, long long part, long long u, int lrow) {
+  return (size_t)(part + u) * a.unit_rows + lrow;
+}
 
 // The prefix of a (sequence, KV head) is streamed as 64-entry chunks: level 0's
 // ceil(n0/64) chunks, then level 1's.  Splits take equal runs of chunks, so a

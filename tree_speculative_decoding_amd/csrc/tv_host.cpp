@@ -15,8 +15,6 @@
 namespace {
 
 thread_local char g_err[512] = "";
-thread_local hipEvent_t g_ev_start = nullptr;
-thread_local hipEvent_t g_ev_stop = nullptr;
 
 tv_status fail(tv_status s, const char* fmt, ...) {
   va_list ap;
@@ -88,10 +86,15 @@ int device_cus() {
 }
 
 struct Plan {
-  int R, unit_rows, row_blocks, tmax, parts, smax;
+  bool mfma;        // bf16 with d = 128 runs the MFMA prefix kernel, everything else the vector kernel
+  bool fused_tree;  // the MFMA kernel attends to the raw tail and the tree chunk itself
+  int tree_tiles;   // 16-entry tiles of that chunk
+  int R, unit_rows, row_blocks, tmax, parts;
   long long units, per;
+  bool all_whole;   // every unit is one workgroup's and the prefix kernel writes the rows: no partials
   size_t ws_o_bytes, ws_ml_off, total;
-  bool fold;  // the MFMA prefix launch has room for the scratch pad's B*D workgroups
+  bool fold;        // the MFMA prefix launch has room for the scratch pad's B*D workgroups ahead of the stream
+  bool pad_after;   // else they follow the stream's workgroups in the same launch
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -99,16 +102,17 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Prefix-stream partition (see AttnArgs).  Auto mode runs one round of persistent
 // workgroups, as many as fit on the device at once (two per CU for both kernels), but
 // keeps at least 4 chunks (256 entries) per workgroup: small prefixes are latency-bound,
-// and spreading them wide pays for partials up to a quarter of the streamed bytes.
+// and spreading them wide pays for partials up to a quarter of the streamed bytes.  The
+// kernel choice is made here once; the launch and the merge follow it.
 Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   Plan p{};
   const int G = Hq / st->Hkv;
   p.R = G * D;
+  p.mfma = st->dtype == TV_BF16 && st->d == 128;
   // the MFMA kernel takes more than 64 rows of a KV head (G*D > 64) in 128-row units of an
   // 8-wave workgroup, one per CU, so the rows share one stream of the prefix; the vector
   // kernel and smaller trees use 64-row units
-  const bool mfma = st->dtype == TV_BF16 && st->d == 128;
-  p.unit_rows = mfma && p.R > 64 ? 128 : 64;
+  p.unit_rows = p.mfma && p.R > 64 ? 128 : 64;
   p.row_blocks = (p.R + p.unit_rows - 1) / p.unit_rows;
   p.tmax = 0;
   for (int l = 0; l < st->n_levels; ++l) p.tmax += (st->lvl[l].cap + 63) / 64;
@@ -117,12 +121,15 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   if (total == 0) {
     p.parts = 0;
     p.per = 1;
-    p.smax = 0;
   } else {
     long long want;
     const bool wide = p.unit_rows == 128;
     const long long slots = (long long)device_cus() * (wide ? 1 : 2);  // workgroups resident at once
     const long long pad = (long long)st->B * D;                        // scratch-pad workgroups
+    // The scratch pad rides in the same launch (of 256-thread workgroups): ahead of the
+    // stream's workgroups when the stream leaves room for it or when it is a handful of
+    // workgroups (taken from the stream's), else behind them, where its short workgroups
+    // fill the slots of the first slices to finish.
     if (num_parts > 0) {
       want = num_parts;
       p.fold = !wide && want + pad <= slots;
@@ -130,8 +137,6 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
       want = slots;
       const long long by_size = (total + 3) / 4;
       if (want > by_size) want = by_size;
-      // the scratch pad rides in the same launch (of 256-thread workgroups) when the stream
-      // leaves room for it, or when it is a handful of workgroups (taken from the stream's)
       if (!wide && want + pad <= slots) {
         p.fold = true;
       } else if (!wide && pad <= 16 && pad < want) {
@@ -139,19 +144,25 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
         p.fold = true;
       }
     }
+    p.pad_after = !wide && !p.fold;
     if (want > total) want = total;
     if (want < 1) want = 1;
     p.per = (total + want - 1) / want;
     p.parts = (int)((total + p.per - 1) / p.per);
-    // a unit starting at offset o < per inside a slice meets floor((o + tmax - 1)/per) + 1 slices
-    long long sm = (p.per + p.tmax - 2) / p.per + 1;
-    if (sm > p.parts) sm = p.parts;
-    p.smax = (int)sm;
   }
-  const size_t rows = (size_t)st->B * st->Hkv * p.smax * p.R;
+  // the tail (< C0 tokens) and the D tree tokens form one extra chunk of at most 64
+  // entries, attended in 16-entry tiles
+  const int c0 = st->n_levels > 0 ? st->lvl[0].C : 1;
+  const int tree_entries = D + (c0 - 1);
+  p.fused_tree = p.mfma && p.parts > 0 && tree_entries <= 64;
+  p.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
+  p.all_whole = p.fused_tree && p.per % p.tmax == 0;
+  // partials: one row block per (slice, unit) pair, numbered slice + unit
+  const size_t rows = p.all_whole || p.parts == 0 ? 0 : (size_t)(p.parts + p.units - 1) * p.unit_rows;
   p.ws_o_bytes = round256(rows * st->d * sizeof(float));
   p.ws_ml_off = p.ws_o_bytes;
   p.total = p.ws_o_bytes + round256(rows * sizeof(float2));
+  if (p.total == 0) p.total = 256;  // a workspace is always asked for (0 reports invalid arguments)
   return p;
 }
 
@@ -202,39 +213,25 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
   if (scratch != nullptr) a.scratch = *scratch;
   a.build_scratch = scratch != nullptr;
   a.unit_rows = p.unit_rows; a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
-  a.smax = p.smax;
-  const int c0 = st->n_levels > 0 ? st->lvl[0].C : 1;
   a.ws_o = (float*)workspace;
   a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
   a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);
-
-  const bool mfma = st->dtype == TV_BF16 && st->d == 128;
-  // the tail (< C0 tokens) and the D tree tokens form one extra chunk of at most 64
-  // entries, attended in 16-entry tiles
-  const int tree_entries = D + (c0 - 1);
-  a.fused_tree = mfma && p.parts > 0 && tree_entries <= 64;
-  a.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
+  a.fused_tree = p.fused_tree;
+  a.tree_tiles = p.tree_tiles;
   // the scratch pad needs only the tree tokens, the plan and the committed open sums: in
   // workgroups of the MFMA prefix launch when it has room, else a short kernel ahead of it
-  a.fold_scratch = (mfma && p.fold && p.parts > 0 && a.build_scratch && st->n_levels > 0) ? st->B * D : 0;
+  a.fold_scratch = (p.mfma && (p.fold || p.pad_after) && p.parts > 0 && a.build_scratch && st->n_levels > 0)
+                       ? st->B * D : 0;
+  a.pad_after = a.fold_scratch > 0 && p.pad_after;
   if (a.fold_scratch == 0) {
     s = hip_check(tv::launch_scratch(a, stream), "scratch pad launch");
     if (s != TV_OK) return s;
   }
-  if (g_ev_start) {
-    s = hip_check(hipEventRecord(g_ev_start, stream), "timing event");
-    if (s != TV_OK) return s;
-  }
-  s = hip_check(mfma ? tv::launch_attn_mfma(a, stream) : tv::launch_attn_valu(a, stream), "prefix attention launch");
+  s = hip_check(p.mfma ? tv::launch_attn_mfma(a, stream) : tv::launch_attn_valu(a, stream), "prefix attention launch");
   if (s != TV_OK) return s;
-  if (g_ev_stop) {
-    s = hip_check(hipEventRecord(g_ev_stop, stream), "timing event");
-    if (s != TV_OK) return s;
-  }
   // nothing left for the finish kernel when every slice is made of whole units: the
   // prefix kernel then wrote every output row itself
-  const bool all_whole = a.fused_tree && p.per % p.tmax == 0;
-  if (all_whole) return ok();
+  if (p.all_whole) return ok();
   return hip_check(tv::launch_attn_finish(a, stream), "attention finish launch");
 }
 
@@ -256,13 +253,6 @@ TV_API const char* tv_status_string(tv_status s) {
 TV_API const char* tv_last_error(void) { return g_err; }
 
 TV_API int tv_version(void) { return TV_VERSION; }
-
-TV_API tv_status tv_set_timing_events(hipEvent_t start, hipEvent_t stop) {
-  if ((start == nullptr) != (stop == nullptr)) return fail(TV_EINVAL, "give both events or neither");
-  g_ev_start = start;
-  g_ev_stop = stop;
-  return ok();
-}
 
 TV_API tv_status tv_build_tree_mask(int B, int D, const int32_t* parents, uint64_t* anc, int32_t* depth,
                                     int32_t* seq_err, hipStream_t stream) {

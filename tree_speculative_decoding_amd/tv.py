@@ -76,7 +76,6 @@ def lib() -> ctypes.CDLL:
             "tv_accept_refresh": ([i32, ctypes.POINTER(TvState), ctypes.POINTER(TvScratch), vp, vp, vp, vp, vp,
                                    vp, vp, vp, vp, vp, vp, vp, vp], i32),
             "tv_compress_prefix": ([ctypes.POINTER(TvState), vp, vp, i32, vp, vp], i32),
-            "tv_set_timing_events": ([vp, vp], i32),
             "tv_build_draft_tree": ([i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
             "tv_draft_attn": ([i32, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(TvState), vp, vp, vp, sz, i32,
                                vp], i32),
@@ -418,18 +417,6 @@ def tv_compress_prefix(st, raw_k: torch.Tensor, raw_v: torch.Tensor, seq_err: to
     max_len = raw_k.shape[2]
     _check(lib().tv_compress_prefix(ctypes.byref(s), _ptr(raw_k), _ptr(raw_v), max_len, _ptr(seq_err),
                                     _stream(stream)))
-
-
-def _event_handle(e):
-    """hipEvent_t of a torch.cuda.Event, or an object carrying a raw `handle`."""
-    if e is None:
-        return None
-    h = getattr(e, "handle", None)
-    return ctypes.c_void_p(h if h is not None else e.cuda_event)
-
-
-def tv_set_timing_events(start, stop) -> None:
-    _check(lib().tv_set_timing_events(_event_handle(start), _event_handle(stop)))
 
 
 def tv_version() -> int:
