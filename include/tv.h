@@ -214,6 +214,27 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
                                 hipStream_t stream);
 
 /*
+ * tv_verify_attn for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * results as tv_verify_attn (the same kernels, bit-identical outputs and scratch pad),
+ * without workspace / workspace_bytes: the split-prefix partials go to a device array
+ * of TV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on until the
+ * process ends (its address is looked up on the first call on each device; nothing is
+ * allocated by any call).  A shape whose partials need more (tv_verify_attn_workspace_bytes
+ * > TV_NOALLOC_SCRATCH_BYTES, i.e. many prefixes split over many slices) returns
+ * TV_EWORKSPACE before any launch.  The array needs no clearing: each call writes every
+ * partial it reads.  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (two streams, two threads) race and give undefined results; calls
+ * ordered on one stream are safe.
+ */
+#define TV_NOALLOC_SCRATCH_BYTES (24u << 20)
+TV_API tv_status tv_verify_attn_noalloc(int D, int Hq, const void* q, const void* k_tree,
+                                        const void* v_tree, const uint64_t* anc, const int32_t* depth,
+                                        const int32_t* seq_err, const tv_state* st,
+                                        const tv_scratch* scratch, void* out, float* lse, int num_parts,
+                                        hipStream_t stream);
+
+/*
  * Branch-aware attention of one draft-decode level (TSD-V4 §4.1: draft decode computes
  * the candidates' representations under the tree topology; §4.3: the same metadata
  * serves draft and verify).  The candidate tree grows level by level in creation order

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -83,6 +84,36 @@ int device_cus() {
     return 256;
   if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// The device memory behind tv_verify_attn_noalloc: one copy of this array on every GPU
+// the library runs on, held until the process ends.  In host code the name `scratch` is a
+// host-side stand-in, not a device address: each device's address is looked up once
+// (hipGetSymbolAddress, with that device current) and only that address is ever used.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[TV_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+tv_status noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cached[kMaxDevices] = {};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TV_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  void* p = cached[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = cached[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(TV_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+      cached[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ok();
 }
 
 struct Plan {
@@ -303,6 +334,28 @@ TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree
   if (depth == nullptr && st != nullptr && st->B > 0) return fail(TV_EINVAL, "NULL pointer argument (depth)");
   return run_attn(D, D, Hq, q, k_tree, v_tree, anc, depth, seq_err, st, scratch, out, lse, workspace,
                   workspace_bytes, num_parts, stream);
+}
+
+TV_API tv_status tv_verify_attn_noalloc(int D, int Hq, const void* q, const void* k_tree, const void* v_tree,
+                                        const uint64_t* anc, const int32_t* depth, const int32_t* seq_err,
+                                        const tv_state* st, const tv_scratch* scratch_pad, void* out, float* lse,
+                                        int num_parts, hipStream_t stream) {
+  if (depth == nullptr && st != nullptr && st->B > 0) return fail(TV_EINVAL, "NULL pointer argument (depth)");
+  tv_status s = check_state(st);
+  if (s != TV_OK) return s;
+  if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
+  if (Hq < 1 || Hq % st->Hkv != 0) return fail(TV_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, st->Hkv);
+  if (num_parts < 0) return fail(TV_EINVAL, "num_parts = %d < 0", num_parts);
+  const size_t need = make_plan(D, Hq, st, num_parts).total;
+  if (need > TV_NOALLOC_SCRATCH_BYTES)
+    return fail(TV_EWORKSPACE, "this shape needs %zu bytes of split-prefix partials; tv_verify_attn_noalloc has %zu "
+                "(use tv_verify_attn with a workspace, or more sequences per call so fewer prefixes are split)",
+                need, (size_t)TV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  s = noalloc_scratch(&ws);
+  if (s != TV_OK) return s;
+  return run_attn(D, D, Hq, q, k_tree, v_tree, anc, depth, seq_err, st, scratch_pad, out, lse, ws,
+                  TV_NOALLOC_SCRATCH_BYTES, num_parts, stream);
 }
 
 TV_API tv_status tv_draft_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree, const void* v_tree,

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
                                    vp, vp, vp, vp, vp, vp, vp, vp], i32),
             "tv_compress_prefix": ([ctypes.POINTER(TvState), vp, vp, i32, vp, vp], i32),
             "tv_build_draft_tree": ([i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+            "tv_verify_attn_noalloc": ([i32, i32, vp, vp, vp, vp, vp, vp, ctypes.POINTER(TvState),
+                                        ctypes.POINTER(TvScratch), vp, vp, i32, vp], i32),
             "tv_draft_attn": ([i32, i32, i32, vp, vp, vp, vp, vp, ctypes.POINTER(TvState), vp, vp, vp, sz, i32,
                                vp], i32),
             "tv_status_string": ([i32], ctypes.c_char_p),
@@ -369,6 +371,19 @@ def tv_verify_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, 
                                 ctypes.byref(sc) if sc is not None else None, _ptr(out), _ptr(lse),
                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
                                 num_parts, _stream(stream)))
+
+
+def tv_verify_attn_noalloc(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, anc: torch.Tensor,
+                           depth: torch.Tensor, seq_err: Optional[torch.Tensor], st, scratch,
+                           out: torch.Tensor, lse: Optional[torch.Tensor], num_parts: int = 0, stream=None) -> None:
+    """tv_verify_attn with the library's own device array for the split-prefix partials."""
+    B, D, Hq, d = q.shape
+    s = _state(st)
+    sc = _scratch(scratch)
+    _check(lib().tv_verify_attn_noalloc(D, Hq, _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(anc), _ptr(depth),
+                                        _ptr(seq_err), ctypes.byref(s),
+                                        ctypes.byref(sc) if sc is not None else None, _ptr(out), _ptr(lse),
+                                        num_parts, _stream(stream)))
 
 
 def tv_draft_attn(q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor, anc: torch.Tensor,
