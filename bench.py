@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--workload", default="high_batch")
     ap.add_argument("--parts", type=int, default=0, help="prefix-stream workgroups (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-in-place", action="store_true",
+                    help="scratch pad without the in-place chain: the refresh copies every committed entry")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the draft-tree, draft-attention and paged-pool measurements (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
@@ -382,7 +384,7 @@ def pooled_state(w, caps, draw_seqs=None):
 class StepRunner:
     """Per-step buffers of one (B, D, Hq) shape and the four calls of one step on `stream`."""
 
-    def __init__(self, w, st, parts: int, stream):
+    def __init__(self, w, st, parts: int, stream, in_place: bool = True):
         import torch
         import tree_speculative_decoding_amd as tv
         B, D, Hq, Hkv, d, dev = st.B, w.D, w.Hq, w.Hkv, w.d, "cuda"
@@ -397,7 +399,7 @@ class StepRunner:
         self.path = torch.zeros(B, D, dtype=torch.int32, device=dev)
         self.bonus = torch.zeros(B, dtype=torch.int32, device=dev)
         self.log = torch.zeros(B, len(w.levels), D, 2, dtype=torch.int32, device=dev)
-        self.sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels))
+        self.sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels), in_place=in_place)
         self.ws = torch.empty(tv.tv_verify_attn_workspace_bytes(D, Hq, st, parts) // 4 + 64, dtype=torch.float32,
                               device=dev)
 
@@ -544,7 +546,7 @@ def main():
     states = [pooled_state(w.with_(B=B * n_rot), caps, range(r * B, (r + 1) * B)) for r in range(n_rot)]
     st = states[0]
     stream = torch.cuda.current_stream()
-    runner = StepRunner(w, st, args.parts, stream)
+    runner = StepRunner(w, st, args.parts, stream, in_place=not args.no_in_place)
     sets = [runner.inputs(t) for t in range(N_INPUT_SETS)]
     saved_all = [snapshot(x) for x in states]
     torch.cuda.synchronize()
@@ -585,6 +587,7 @@ def main():
         "config": {"workload": w.name, "B": B, "D": D, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.d,
                    "prefix_tokens": w.P, "levels": list(w.levels), "tree": w.spec_name,
                    "p_agree": w.p_agree, "prefix_workgroups": args.parts or "auto",
+                   "refresh_skip": "off" if args.no_in_place else "in-place chain",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
@@ -682,6 +685,7 @@ def sweep(args) -> None:
     steps, warmup = args.steps, args.warmup
     ceiling = read_ceiling(stream)
     rows = []
+    oracle_rows = {}
     for B in sorted({w.B for w in points}):
         ws_ = [w for w in points if w.B == B]
         w0 = ws_[0]
@@ -735,7 +739,15 @@ def sweep(args) -> None:
             del runner, sets
         del states, saved
         torch.cuda.empty_cache()
-    write_sweep_table(args, rows, ceiling)
+        # the oracle beside the GPU: a time-budgeted sample of this batch size's D = 8, top-k 2
+        # point on the host's cores (per-sequence work, so its tokens/s does not depend on B)
+        if not args.no_cpu_baseline:
+            w8 = [w for w in ws_ if w.D == 8 and w.topk == 2][0]
+            ob = cpu_baseline(w8, args.cpu_seconds)
+            ob["point"] = w8.name
+            oracle_rows[B] = ob
+            print(json.dumps({"oracle_B": B, **ob}), flush=True)
+    write_sweep_table(args, rows, ceiling, oracle_rows)
 
 
 def graph_step_ms(runner: StepRunner, sts: list, sets: list, steps: int, states: list, saved: list) -> float:
@@ -851,7 +863,7 @@ def restore(st, sv: dict) -> None:
         dst.copy_(src)
 
 
-def write_sweep_table(args, rows: list, ceiling: dict) -> None:
+def write_sweep_table(args, rows: list, ceiling: dict, oracle_rows: dict) -> None:
     hdr = ["# Long-context budget sweep: verify step at a 131072-token prefix", "",
            "64/8 heads, d=128, bf16, 32768 C4 + 1024 C128 committed entries per sequence; one step = plan,",
            "verify attention with the scratch pad, accept, refresh.  Command (repository root):", "",
@@ -866,8 +878,9 @@ def write_sweep_table(args, rows: list, ceiling: dict) -> None:
            "attention flops per algorithmic byte; graph = the same steps replayed from one captured HIP "
            "graph; graph fused = the same with tv_accept_refresh in place of tv_accept + tv_refresh_state.", "",
            "| D | B | top-k | p | mode | intensity | attn us (p10-p90) | attn GB/s | % of 8 TB/s | % of ceiling "
-           "| step us | verified tok/s | graph step us | graph tok/s | graph fused step us | accepted length |",
-           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+           "| step us | verified tok/s | graph step us | graph tok/s | graph fused step us | accepted length "
+           "| oracle tok/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     body = []
     for r in sorted(rows, key=lambda r: (r["B"], r["D"], r["topk"], r["p_agree"], r["mode"])):
         p10, _, p90 = r["attn_us_p10_p50_p90"]
@@ -876,9 +889,15 @@ def write_sweep_table(args, rows: list, ceiling: dict) -> None:
                     f"{100 * r['attn_frac_of_peak']:.1f} | {100 * r['attn_frac_of_ceiling']:.1f} | {r['step_us']} | "
                     f"{r['verified_tokens_per_s']:.0f} | {r.get('graph_step_us', '-')} | "
                     f"{r.get('graph_verified_tokens_per_s', '-')} | {r.get('graph_fused_step_us', '-')} | "
-                    f"{r['accepted_length']} |")
+                    f"{r['accepted_length']} | {oracle_rows[r['B']]['value'] if r['B'] in oracle_rows else '-'} |")
+    foot = ["", "Oracle (the fp64 CPU definition, as it stands) beside the GPU, same run, same host: per batch "
+            "size, whole sequences of its D = 8, top-k 2, p = 0.5 point until the time budget is spent "
+            "(one full step each; the oracle's work is per sequence, so its tokens/s does not depend on B):", ""]
+    for B, ob in sorted(oracle_rows.items()):
+        foot.append(f"- B = {B}: {ob['value']} tokens/s on {ob['cores']} cores ({ob['blas']} BLAS, "
+                    f"{ob['blas_threads']} threads); {ob['sample']}")
     with open(args.sweep, "w") as fh:
-        fh.write("\n".join(hdr + body) + "\n")
+        fh.write("\n".join(hdr + body + (foot if oracle_rows else [])) + "\n")
 
 
 def time_draft_tree(w, steps: int, stream) -> dict:
@@ -1037,6 +1056,7 @@ def cpu_baseline(w, budget_s: float):
         blas = ",".join(sorted({str(i.get("internal_api")) for i in info if i.get("user_api") == "blas"})) or "none"
     except Exception:
         threads, blas = 1, "unknown"
+    cores = len(os.sched_getaffinity(0))
     caps = [w.P // C + 64 for C in w.levels]
     done, t_used = 0, 0.0
     b = 0
@@ -1052,7 +1072,8 @@ def cpu_baseline(w, budget_s: float):
         t_used += time.perf_counter() - t0
         done += 1
         b += 1
-    return {"value": round(done * w.D / t_used, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle", "blas": blas,
+    return {"value": round(done * w.D / t_used, 2), "unit": "tokens/s", "cores": cores, "blas_threads": threads,
+            "kind": "oracle", "blas": blas,
             "sample": f"{done} of {w.B} sequences of {w.name}, one full step each (plan, attention, scratch, "
                       f"accept, refresh), fp64 numpy; input widening excluded; {t_used:.1f} s"}
 

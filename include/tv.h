@@ -128,12 +128,25 @@ typedef struct {
 /* Per-branch temporary compression results (TSD-V4 §4.2 scratch pad), per level l:
  * entry for node i is valid only if node i closes a block of that level, i.e.
  * (P + depth(i) + 1) % C == 0; open sums are the open block after node i along
- * its own chain (zero where it closes).  Overwritten by every tv_verify_attn. */
+ * its own chain (zero where it closes).  Overwritten by every tv_verify_attn.
+ *
+ * in_place (optional; TSD-V4 §4.3: with a single candidate chain, or when the accepted
+ * chain is the one already cached, the refresh can be skipped): when non-NULL,
+ * tv_verify_attn also writes the entries that the nodes of one chain close straight into
+ * their pool slots -- the chain ending at the deepest node, smallest index among equals
+ * (the path full acceptance selects; the whole tree when it is a single chain) -- and sets
+ * in_place[b] to that chain's node mask (0 for a flagged sequence).  Those slots lie at
+ * or beyond the committed counts, so the committed state does not change, and only slots
+ * below the capacity whose page exists are written.  tv_refresh_state / tv_accept_refresh
+ * given the same struct then copy only the committed entries of nodes outside the mask.
+ * The resulting state is bit-identical to the one without in_place, apart from pool
+ * slots at or beyond the new counts (never read). */
 typedef struct {
   void* entry_k[TV_MAX_LEVELS];   /* [B][D][Hkv][d] element dtype */
   void* entry_v[TV_MAX_LEVELS];   /* [B][D][Hkv][d] */
   float* open_k[TV_MAX_LEVELS];   /* [B][D][Hkv][d] fp32 */
   float* open_v[TV_MAX_LEVELS];   /* [B][D][Hkv][d] */
+  uint64_t* in_place;             /* [B] out of tv_verify_attn, in to the refresh; NULL = off */
 } tv_scratch;
 
 /*
@@ -284,6 +297,9 @@ TV_API tv_status tv_accept(int B, int D, const int32_t* parents, const uint64_t*
  *   seq_err [B] in/out: skipped if nonzero; set to TV_SEQ_POOL_FULL (state untouched)
  *              if a level would exceed its capacity, TV_SEQ_BAD_PATH if m >= D or a
  *              path node is outside 0..D-1 (state untouched)
+ * "State untouched" means P, the counts, open sums, tail and every committed pool slot;
+ * with scratch->in_place the verify may already have written slots at or beyond the
+ * committed counts, which nothing reads until a later refresh commits them.
  */
 TV_API tv_status tv_refresh_state(int D, const tv_state* st, const tv_scratch* scratch,
                                   const void* k_tree, const void* v_tree, const int32_t* m,

@@ -24,7 +24,7 @@ def test_struct_layout_matches_header():
     assert tv.tv.TvLevel.page_table.offset == 48 and tv.tv.TvLevel.num_pages.offset == 60
     assert ctypes.sizeof(TvState) == 176
     assert TvState.lvl.offset == 24 and TvState.P.offset == 168
-    assert ctypes.sizeof(TvScratch) == 64
+    assert ctypes.sizeof(TvScratch) == 72 and TvScratch.in_place.offset == 64
 
 
 def fake_state(**kw):

@@ -111,9 +111,13 @@ def test_rejected_branches_never_reach_state():
     assert torch.equal(a.tail_k.view(torch.int16), b.tail_k.view(torch.int16))
 
 
-def test_pool_full_leaves_sequence_unchanged():
+@pytest.mark.parametrize("in_place", [False, True])
+def test_pool_full_leaves_sequence_unchanged(in_place):
+    """A sequence whose commit would overflow a pool is flagged and keeps its committed
+    state; without the in-place chain not a byte of its pools changes, with it the verify
+    may have written slots at or beyond the committed count (never read), nothing below."""
     import torch
-    _say("refresh pool full")
+    _say(f"refresh pool full (in place: {in_place})")
     w = synth.Workload("full", 3, 8, 8, 1, 64, "f32", (4,), 60, 1, 7, 1.0, 3200, prefix="raw")
     # capacity 64 entries = 256 tokens; sequences start at 60 tokens (15 entries)
     dst = device_state(w, [64])
@@ -124,7 +128,7 @@ def test_pool_full_leaves_sequence_unchanged():
     tv.tv_compress_prefix(dst, tv.to_device(rk, "f32"), tv.to_device(rk, "f32"), err)
     torch.cuda.synchronize()
     before = [t.clone() for t in (dst.P, dst.n[0], dst.logical_k(0), dst.open_k[0], dst.tail_k)]
-    r = Runner(dst, w.D, w.Hq)
+    r = Runner(dst, w.D, w.Hq, in_place=in_place)
     s = synth.step_inputs(w, 0)
     x = upload_step(s, w.dtype)
     r.step(x)
@@ -139,7 +143,9 @@ def test_pool_full_leaves_sequence_unchanged():
     for b in (1, 2):
         assert P[b] == before[0][b].item()
         assert dst.n[0][b].item() == before[1][b].item()
-        assert torch.equal(dst.logical_k(0)[b], before[2][b])
+        n = before[1][b].item()
+        lim = None if not in_place else n  # committed slots only when the chain is written in place
+        assert torch.equal(dst.logical_k(0)[b][:, :lim], before[2][b][:, :lim])
         assert torch.equal(dst.open_k[0][b], before[3][b])
         assert torch.equal(dst.tail_k[b], before[4][b])
 
@@ -194,6 +200,85 @@ def _one_seq(st: oracle.State, b: int) -> oracle.State:
     return oracle.State(st.levels, [pick(a) for a in st.pool_k], [pick(a) for a in st.pool_v],
                         [pick(a) for a in st.n], [pick(a) for a in st.open_k], [pick(a) for a in st.open_v],
                         pick(st.tail_k), pick(st.tail_v), pick(st.P))
+
+
+IN_PLACE = {
+    # single chains (top-k = 1): every committed entry is already in its slot
+    "bf16_chain_c4_c128": (synth.Workload("ip1", 3, 8, 16, 2, 128, "bf16", (4, 128), 125, 1, 7, 0.9, 3401, prefix="raw"), 40),
+    "f32_chain_c2_c8": (synth.Workload("ip2", 2, 6, 8, 2, 64, "f32", (2, 8), 13, 1, 5, 0.8, 3402, prefix="raw"), 30),
+    # trees: only the deepest chain is written in place, other accepted nodes are copied
+    "bf16_tree_c4_c128": (synth.Workload("ip3", 4, 8, 16, 2, 128, "bf16", (4, 128), 122, 2, 3, 0.7, 3403, prefix="raw"), 40),
+    "bf16_tree_c1_c4": (synth.Workload("ip4", 2, 8, 8, 1, 128, "bf16", (1, 4), 9, 2, 3, 0.8, 3404, prefix="raw"), 25),
+}
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("name,fused,paged", [(n, False, False) for n in IN_PLACE] +
+                         [("bf16_tree_c4_c128", True, False), ("bf16_chain_c4_c128", False, True)])
+def test_in_place_chain_equals_copy_path(name, fused, paged):
+    """The refresh skip (TSD-V4 §4.3): with scratch.in_place the verify writes the deepest
+    chain's closing entries straight into their pool slots and the refresh copies only the
+    other accepted nodes' entries.  Step after step the run matches the run without it bit
+    for bit -- acceptance, commit log, status, counts, open sums, tails and every committed
+    pool entry -- and the oracle; in_place[b] is the chain of the deepest node (smallest
+    index among equals), the whole tree for a single chain."""
+    import torch
+    w, T = IN_PLACE[name]
+    _say(f"in-place chain {name} fused={fused} paged={paged}: {T} steps")
+    caps = pooled_caps(w, T * w.D + 8)
+    page_seed = 21 if paged else None
+    runs = []
+    for in_place in (False, True):
+        dst = device_state(w, caps, poison=True, page_seed=page_seed, spare_pages=3 if paged else 0)
+        runs.append((dst, Runner(dst, w.D, w.Hq, in_place=in_place)))
+    (da, ra), (db, rb) = runs
+    ost = oracle_state(w, caps)
+    for t in range(T):
+        s = synth.step_inputs(w, t)
+        h = widen_step(s, w.dtype)
+        for dst, r in runs:
+            x = upload_step(s, w.dtype)
+            r.step(x, fused=fused)
+        torch.cuda.synchronize()
+        ref = oracle.step(ost, s.parents, s.draft, s.target, h.q, h.kt, h.vt)
+        # the in-place mask: the chain of the deepest node, smallest index among equals
+        anc, depth, _ = oracle.build_plan(s.parents)
+        want = []
+        for b in range(w.B):
+            leaf = int(np.lexsort((np.arange(w.D), -depth[b]))[0])
+            want.append(int(oracle.anc_to_bits(anc[b, leaf][None])[0]))
+        assert (rb.sc.in_place.cpu().numpy().view(np.uint64) == np.array(want, dtype=np.uint64)).all(), f"step {t}"
+        if w.topk == 1:
+            assert all(v == (1 << w.D) - 1 for v in want)
+        for name_ in ("m", "path", "bonus", "log", "err"):
+            assert torch.equal(getattr(ra, name_), getattr(rb, name_)), f"step {t} {name_}"
+        assert torch.equal(_bits(ra.out), _bits(rb.out)), f"step {t} attention"
+        assert (rb.m.cpu().numpy() == ref.m).all() and (rb.path.cpu().numpy() == ref.path).all()
+        assert torch.equal(da.P, db.P)
+        for l in range(len(w.levels)):
+            assert torch.equal(da.n[l], db.n[l])
+            assert torch.equal(da.open_k[l], db.open_k[l]) and torch.equal(da.open_v[l], db.open_v[l])
+            n = da.n[l].cpu().numpy()
+            ka, kb = da.logical_k(l), db.logical_k(l)
+            va = tv_untile(da.logical_vt(l))
+            vb = tv_untile(db.logical_vt(l))
+            for b in range(w.B):
+                assert torch.equal(_bits(ka[b, :, :n[b]]), _bits(kb[b, :, :n[b]])), f"step {t} level {l} K"
+                assert torch.equal(_bits(va[b, :, :n[b]]), _bits(vb[b, :, :n[b]])), f"step {t} level {l} V"
+        if da.tail_k is not None:
+            assert torch.equal(_bits(da.tail_k), _bits(db.tail_k)) and torch.equal(_bits(da.tail_v), _bits(db.tail_v))
+        ost = ref.state
+    compare_state(db, ost, w.dtype, f"{name} in place, final state")
+
+
+def tv_untile(vt):
+    """[B][Hkv][T][d][64] V tiles -> [B][Hkv][T*64][d] (layout only)."""
+    B, H, T, d, A = vt.shape
+    return vt.transpose(-1, -2).reshape(B, H, T * A, d)
 
 
 FUSED = {

@@ -76,3 +76,16 @@ def test_long_context_batch64_sampled():
     """Batch 64, D=5 (40 query rows per KV head, a partial MFMA row block): 8.9 GB of
     compressed pools, one whole (sequence, KV head) prefix per workgroup."""
     _full_step(_point(5, 2, 64, 0.7), [0, 41, 63])
+
+
+def test_long_context_batch16_split():
+    """Batch 16, D=7 chains: 128 (sequence, KV head) prefixes over about 500 workgroups, so
+    every prefix is split over several slices and merged; sampled sequences."""
+    _full_step(_point(7, 1, 16, 0.7), [0, 7, 15])
+
+
+def test_long_context_batch64_d8_sampled():
+    """Batch 64, D=8 (64 query rows per KV head, whole MFMA row blocks), top-k 2: one
+    whole prefix per workgroup, the scratch pad's workgroups behind the stream's."""
+    _full_step(_point(8, 2, 64, 0.5), [0, 63])
+

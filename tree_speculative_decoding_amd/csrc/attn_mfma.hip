@@ -43,14 +43,34 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 namespace {
 constexpr int kDH = 128;        // head dim handled by this kernel
 constexpr int kChunk = 64;      // entries per chunk
-constexpr int kKStr = kDH * 2 + 16;      // LDS bytes per K row (padded)
-constexpr int kVStr = kChunk * 2 + 16;   // LDS bytes per V^T row (padded)
-constexpr int kLdsBytes = kChunk * kKStr + kDH * kVStr;
+// LDS layouts, chosen by measuring ds_read_b128 on gfx950 (64 banks): under load a row
+// stride of an odd number of 16-byte units (272 B for K, 144 B for V^T) costs 1.6x the
+// cycles of a conflict-free read, an even number (288 B) or an XOR swizzle does not.
+constexpr int kKStr = kDH * 2 + 32;      // LDS bytes per K row (padded to 18 units of 16 B)
+constexpr int kVStr = kChunk * 2;        // LDS bytes per V^T row (unpadded, 16-byte units swizzled)
+// the V area also holds the tree chunk's V rows, entry-major with the K row stride
+constexpr int kVBytes = kDH * kVStr > kChunk * kKStr ? kDH * kVStr : kChunk * kKStr;
+constexpr int kLdsBytes = kChunk * kKStr + kVBytes;
 // LDS slot of entry e (0..63) within a V^T row.  The P^T operand of the PV product gives
 // lane group grp the entries 32h + 4grp + {0..3} and 32h + 16 + 4grp + {0..3} of k-step h;
 // storing them at slots 32h + 8grp + {0..7} makes each operand one 16-byte LDS read.
 __device__ __forceinline__ int v_slot(int e) {
   return (e & 32) + 8 * ((e & 15) >> 2) + 4 * ((e >> 4) & 1) + (e & 3);
+}
+// Byte offset of slot s of V^T row r: 16-byte unit s/8 of the row is stored at unit
+// (s/8) ^ (r & 7), so the 16 rows one operand read touches fall in distinct bank groups.
+__device__ __forceinline__ int vt_byte(int r, int s) {
+  return r * kVStr + ((((s >> 3) ^ (r & 7)) << 4) | ((s & 7) << 1));
+}
+// Maximum of v over lanes l and l ^ 16, and then over l ^ 32: gfx950's permlane swaps
+// (v_permlane16_swap / v_permlane32_swap, vector ALU) return the two 16-lane (32-lane)
+// halves of each pair, so the larger of the two results is the pair's maximum in every
+// lane -- no trip through the LDS crossbar as for a general shuffle.
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 // One 16-byte piece of a pool tile, loaded with the nontemporal hint (the `nt` cache
 // policy): a launch reads each tile exactly once, so the caches need not keep it.  On
@@ -95,7 +115,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
   if (NW == 4 && (int)blockIdx.x >= pad0 && (int)blockIdx.x < pad0 + a.fold_scratch) {
     const int item = blockIdx.x - pad0;
     const int sb = item / a.D;
-    scratch_node<uint16_t, 4>(a, sb, item - sb * a.D, (int*)smem);  // (4: no spill beside the stream's registers)
+    scratch_node<uint16_t, 4>(a, sb, item - sb * a.D, (ScratchLds*)smem);  // (4: no spill beside the stream's registers)
     return;
   }
   const int part = a.pad_after ? (int)blockIdx.x : (int)blockIdx.x - a.fold_scratch;  // this workgroup's slice
@@ -207,9 +227,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
           // V^T piece: entries 8k..8k+7 of channel row p/8; its two halves go to their
           // slots in the lane order of the P^T operand (see v_slot)
           const int k8 = (p & 7) * 8;
-          char* vrow = Vs + (p >> 3) * kVStr;
-          *(uint2*)(vrow + v_slot(k8) * 2) = make_uint2(vpre[x].x, vpre[x].y);
-          *(uint2*)(vrow + v_slot(k8 + 4) * 2) = make_uint2(vpre[x].z, vpre[x].w);
+          *(uint2*)(Vs + vt_byte(p >> 3, v_slot(k8))) = make_uint2(vpre[x].x, vpre[x].y);
+          *(uint2*)(Vs + vt_byte(p >> 3, v_slot(k8 + 4))) = make_uint2(vpre[x].z, vpre[x].w);
         }
       }
     };
@@ -246,8 +265,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
                        fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
       mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
                            fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_xor16_32(mx);
       // a row with every score hidden keeps its state (its max stays -inf, p = 0)
       const float m_new = fmaxf(m_run, mx * a.scale_log2);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -275,10 +293,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       // and 32h + 16 + 4grp + {0..3}
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const char* vrow = Vs + (16 * dt + n16) * kVStr;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const bf16x8 vop = *(const bf16x8*)(vrow + (32 * h + 8 * grp) * 2);
+          const bf16x8 vop = *(const bf16x8*)(Vs + vt_byte(16 * dt + n16, 32 * h + 8 * grp));
           oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[h], oacc[dt], 0, 0, 0);
         }
       }
@@ -419,8 +436,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
         for (int t = 0; t < TT; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[t][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = max_xor16_32(mx);
         const float m_new = fmaxf(m_run, mx * a.scale_log2);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);

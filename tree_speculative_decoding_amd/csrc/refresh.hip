@@ -6,12 +6,13 @@
 //
 // One workgroup per sequence, one thread per (KV head, channel) up to 1024; the
 // accepted path is staged in LDS and checked once, and so are the pages the commits
-// write (paged pools: a missing page leaves the sequence unchanged, TV_SEQ_BAD_PAGE).  Every committed element is a bit
-// copy: scratch
-// entries of the path nodes that close a block go to the next pool slots, the
-// path leaf's open-block sums replace the open sums, path tokens extend the raw
-// tail.  Counters (P, n) are written after a barrier, once every thread of the
-// sequence has read the old values.  Rejected nodes are never read.
+// write (paged pools: a missing page leaves the sequence unchanged, TV_SEQ_BAD_PAGE).
+// Every committed element is a bit copy: scratch entries of the path nodes that close a
+// block go to the next pool slots (except those the verify already wrote there: nodes of
+// the scratch pad's in-place chain, TSD-V4 §4.3's refresh skip), the path leaf's
+// open-block sums replace the open sums, path tokens extend the raw tail.  Counters (P,
+// n) are written after a barrier, once every thread of the sequence has read the old
+// values.  Rejected nodes are never read.
 #include "accept_path.h"
 #include "tv_launch.h"
 
@@ -26,6 +27,8 @@ struct RefreshLds {
   // element offset of the block's tile for KV head 0, and from one head's tile to the
   // next (tile_offset is linear in the head in every pool layout)
   size_t it_tile0[kMaxCommits], it_gstep[kMaxCommits];
+  int cp[kMaxCommits];  // the listed commits to copy (those not already in place), any order
+  int ncp;
   int bad;
 };
 
@@ -55,11 +58,12 @@ constexpr int kTailBatch = 4;
 // path and the pages; then each thread copies its channels of every listed entry, the
 // leaf's open sums and the new tail tokens, with all of a batch's loads issued before its
 // stores (the sources, scratch pad and tree tokens, are never written here).
+// `in_place` is the mask of nodes whose entries the verify wrote into the pools (0: none).
 template <typename T>
 __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, const tv_scratch& sc,
                                              const T* __restrict__ k_tree, const T* __restrict__ v_tree, int m,
-                                             int P, RefreshLds& sh, int32_t* __restrict__ commit_log,
-                                             int32_t* __restrict__ seq_err) {
+                                             int P, uint64_t in_place, RefreshLds& sh,
+                                             int32_t* __restrict__ commit_log, int32_t* __restrict__ seq_err) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int L = st.n_levels;
   const int Hkv = st.Hkv, d = st.d, HD = Hkv * d;
@@ -89,12 +93,15 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
     const size_t t0 = tile_offset(paged, page, lv.cap, st.B, Hkv, d, b, 0, j >> 6);
     sh.it_l[i] = l1 ? 1 : 0;
     sh.it_j[i] = j;
-    sh.it_u[i] = sh.pth[j * C + C - 1 - P];  // path node at the block's last position
+    const int u = sh.pth[j * C + C - 1 - P];  // path node at the block's last position
+    sh.it_u[i] = u;
+    if (!((in_place >> (u & 63)) & 1ull) || u < 0) sh.cp[atomicAdd(&sh.ncp, 1)] = i;  // not yet in its slot
     sh.it_tile0[i] = t0;
     sh.it_gstep[i] = tile_offset(paged, page, lv.cap, st.B, Hkv, d, b, 1, j >> 6) - t0;
   }
   __syncthreads();
   const int bad = sh.bad;
+  const int ncp = sh.ncp;
   if (bad != 0 || full) {  // uniform; the state is left unchanged
     if (tid == 0) seq_err[b] = (bad & 1) ? TV_SEQ_BAD_PATH : full ? TV_SEQ_POOL_FULL : TV_SEQ_BAD_PAGE;
     return;
@@ -146,10 +153,10 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
       }
     }
     uint32_t ck[kCommitBatch], cv[kCommitBatch];
-    for (int c0 = 0; c0 < ncom; c0 += kCommitBatch) {
+    for (int c0 = 0; c0 < ncp; c0 += kCommitBatch) {
 #pragma unroll
       for (int t = 0; t < kCommitBatch; ++t) {
-        const int i = c0 + t < ncom ? c0 + t : c0;
+        const int i = sh.cp[c0 + t < ncp ? c0 + t : c0];
         const bool l1 = sh.it_l[i] != 0;
         const size_t src = (seq_rows + sh.it_u[i]) * HD + e;
         ck[t] = Bits<T>::ld(l1 ? ek1 : ek0, src);
@@ -160,8 +167,8 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
                    "v"(cv[7]));
 #pragma unroll
       for (int t = 0; t < kCommitBatch; ++t)
-        if (c0 + t < ncom) {  // uniform
-          const int i = c0 + t, j = sh.it_j[i];
+        if (c0 + t < ncp) {  // uniform
+          const int i = sh.cp[c0 + t], j = sh.it_j[i];
           const tv_level& lv = sh.it_l[i] != 0 ? st.lvl[1] : st.lvl[0];
           const size_t tb = sh.it_tile0[i] + (size_t)g * sh.it_gstep[i];
           Bits<T>::st((T*)lv.k, tb + (size_t)(j & 63) * d + dd, ck[t]);
@@ -219,13 +226,17 @@ __global__ __launch_bounds__(1024) void k_refresh(int D, tv_state st, tv_scratch
   const int m = m_in[b];
   const int P = st.P[b];
   const int pv = tid < D ? path[(size_t)b * D + tid] : -1;
+  const uint64_t in_place = sc.in_place != nullptr ? sc.in_place[b] : 0ull;
   if (commit_log != nullptr)
     for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
   if (tid < D) sh.pth[tid] = pv;
-  if (tid == 0) sh.bad = 0;
+  if (tid == 0) {
+    sh.bad = 0;
+    sh.ncp = 0;
+  }
   __syncthreads();  // log prefill and the reads above happen before any later write
   if (err != TV_SEQ_OK || m < 0) return;
-  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, sh, commit_log, seq_err);
+  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, in_place, sh, commit_log, seq_err);
 }
 
 // Acceptance and refresh in one launch (one workgroup per sequence): the first wave
@@ -254,12 +265,14 @@ __global__ __launch_bounds__(1024) void k_accept_refresh(int D, tv_state st, tv_
     for (int e = tid; e < L * D * 2; e += nt) commit_log[(size_t)b * L * D * 2 + e] = -1;
   const int err = seq_err[b];
   const int P = st.P[b];
+  const uint64_t in_place = sc.in_place != nullptr ? sc.in_place[b] : 0ull;
   if (tid < 64) {  // the first wave: every path slot -1, then the accepted path
     if (tid < D) sh.pth[tid] = -1;
     const int m = accept_one(b, D, parents, anc, depth, draft, target, seq_err, m_out, path, bonus, sh.pth);
     if (tid == 0) {
       m_s = m;
       sh.bad = 0;
+      sh.ncp = 0;
     }
   }
   __syncthreads();  // the path is in LDS; the log prefill and the reads above are done
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(1024) void k_accept_refresh(int D, tv_state st, tv_
   if (err != TV_SEQ_OK || m < 0) return;
   // slots 0..m hold one node each for a plan from tv_build_tree_mask; refresh_body
   // checks them as it checks a path it is given
-  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, sh, commit_log, seq_err);
+  refresh_body<T>(b, D, st, sc, k_tree, v_tree, m, P, in_place, sh, commit_log, seq_err);
 }
 
 hipError_t launch_accept_refresh(int D, const tv_state& st, const tv_scratch& sc, const int32_t* parents,

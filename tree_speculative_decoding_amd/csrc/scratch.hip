@@ -8,9 +8,9 @@ namespace tv {
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_scratch(AttnArgs a) {
-  __shared__ int dep_s[TV_MAX_D];
+  __shared__ ScratchLds sl;
   const int b = blockIdx.x / a.D;
-  scratch_node<T>(a, b, blockIdx.x - b * a.D, dep_s);
+  scratch_node<T>(a, b, blockIdx.x - b * a.D, &sl);
 }
 
 hipError_t launch_scratch(const AttnArgs& a, hipStream_t s) {

@@ -11,6 +11,16 @@
 // (rounded once to the element type) and a zero open sum; any other node writes the
 // running sum.
 //
+// In-place chain (TSD-V4 §4.3: with one candidate chain, or when the accepted chain is the
+// one already cached, the refresh can be skipped).  When the caller gives
+// scratch.in_place, the nodes of one chain -- the path that full acceptance selects, ending
+// at the deepest node (smallest index among equals), i.e. the whole tree when it is a
+// single chain -- also write the entries they close straight into their pool slots
+// (slot j = pos / C >= the committed count, so nothing committed changes and the stream
+// never reads them), provided the slot is below the capacity and its page exists; node 0's
+// workgroup records that chain in in_place[b].  The refresh then copies only the entries
+// of accepted nodes off that chain.  The values are the scratch entries' bits.
+//
 // The pad depends on the tree tokens, the plan and the committed open sums only, not on
 // the prefix: one workgroup per (sequence, node), either in a short kernel of its own
 // ahead of the prefix stream or as extra workgroups of the prefix kernel's launch when
@@ -68,23 +78,51 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// The scratch pad of node i of sequence b, by one workgroup of 256 threads; dep_s is
-// TV_MAX_D ints of LDS.  kBatch chain nodes' loads are issued together.
+// LDS of a scratch-pad workgroup: the tree's depths and chains.
+struct ScratchLds {
+  int dep[TV_MAX_D];
+  uint64_t anc[TV_MAX_D];
+};
+
+// The scratch pad of node i of sequence b, by one workgroup of 256 threads.  kBatch chain
+// nodes' loads are issued together.
 template <typename T, int kBatch = 8>
-__device__ __forceinline__ void scratch_node(const AttnArgs& a, int b, int i, int* dep_s) {
+__device__ __forceinline__ void scratch_node(const AttnArgs& a, int b, int i, ScratchLds* sl) {
   const int tid = threadIdx.x;
   // every load that needs no other load's result goes out in one round trip (issued by
-  // every lane, without branches): the depths, the status, P, the node's chain
+  // every lane, without branches): the depths and chains, the status, P, the node's chain
   const int dval = a.depth[(size_t)b * a.anc_ld + (tid < a.D ? tid : 0)];
+  const uint64_t aval = a.anc[(size_t)b * a.anc_ld + (tid < a.D ? tid : 0)];
   const int eval = *(a.seq_err != nullptr ? a.seq_err + b : a.P + b);
   const int P = a.P[b];
   const uint64_t chain = a.anc[(size_t)b * a.anc_ld + i] & node_mask(a.D);
-  // (an empty use of all four: the compiler issues them together and waits once, instead
-  // of moving each load down to its first use)
-  asm volatile("" ::"v"(dval), "v"(eval), "v"(P), "v"((uint32_t)chain), "v"((uint32_t)(chain >> 32)));
-  if (tid < a.D) dep_s[tid] = dval;
+  // (an empty use of all of them: the compiler issues them together and waits once,
+  // instead of moving each load down to its first use)
+  asm volatile("" ::"v"(dval), "v"(eval), "v"(P), "v"((uint32_t)chain), "v"((uint32_t)(chain >> 32)),
+               "v"((uint32_t)aval), "v"((uint32_t)(aval >> 32)));
+  if (tid < a.D) {
+    sl->dep[tid] = dval;
+    sl->anc[tid] = aval & node_mask(a.D);
+  }
   __syncthreads();
-  if (a.seq_err != nullptr && eval != TV_SEQ_OK) return;  // uniform
+  const bool ok = a.seq_err == nullptr || eval == TV_SEQ_OK;
+  uint64_t* in_place = a.scratch.in_place;
+  if (!ok) {  // uniform
+    if (in_place != nullptr && i == 0 && tid == 0) in_place[b] = 0ull;
+    return;
+  }
+  int* dep_s = sl->dep;
+  // the in-place chain: the deepest node, smallest index among equals (every thread scans
+  // the depths in LDS), and its chain
+  bool on_chain = false;
+  if (in_place != nullptr) {
+    int leaf = 0;
+    for (int u = 1; u < a.D; ++u)
+      if (dep_s[u] > dep_s[leaf]) leaf = u;
+    const uint64_t lchain = sl->anc[leaf];
+    on_chain = (lchain >> i) & 1ull;
+    if (i == 0 && tid == 0) in_place[b] = lchain;
+  }
 
   const int pos = P + dep_s[i];
   int b0[TV_MAX_LEVELS];
@@ -159,10 +197,28 @@ __device__ __forceinline__ void scratch_node(const AttnArgs& a, int b, int i, in
       const size_t dst = ((size_t)b * a.D + i) * HD + e;
       if ((pos + 1) % C == 0) {
         const float cf = (float)C;
-        Quad<T>::store((T*)a.scratch.entry_k[l], dst, make_float4(ks.x / cf, ks.y / cf, ks.z / cf, ks.w / cf));
-        Quad<T>::store((T*)a.scratch.entry_v[l], dst, make_float4(vs.x / cf, vs.y / cf, vs.z / cf, vs.w / cf));
+        const float4 ek = make_float4(ks.x / cf, ks.y / cf, ks.z / cf, ks.w / cf);
+        const float4 ev = make_float4(vs.x / cf, vs.y / cf, vs.z / cf, vs.w / cf);
+        Quad<T>::store((T*)a.scratch.entry_k[l], dst, ek);
+        Quad<T>::store((T*)a.scratch.entry_v[l], dst, ev);
         *(float4*)(a.scratch.open_k[l] + dst) = z;
         *(float4*)(a.scratch.open_v[l] + dst) = z;
+        const int j = pos / C;  // the pool slot this block would be committed to
+        if (on_chain && j < a.cap[l]) {  // uniform
+          const bool paged = a.pt[l] != nullptr;
+          int page = 0;
+          if (paged) page = a.pt[l][(size_t)b * a.ppseq[l] + (j >> 6)];
+          if (!paged || (page >= 0 && page < a.npages[l])) {
+            const int g = e / a.d, c = e - g * a.d;  // four channels of one head
+            const size_t tb = tile_offset(paged, page, a.cap[l], a.B, a.Hkv, a.d, b, g, j >> 6);
+            Quad<T>::store((T*)a.pk[l], tb + (size_t)(j & 63) * a.d + c, ek);
+            T* vt = (T*)a.pvt[l] + tb + (size_t)c * 64 + (j & 63);
+            Elem<T>::store(vt, 0, ev.x);
+            Elem<T>::store(vt, 64, ev.y);
+            Elem<T>::store(vt, 128, ev.z);
+            Elem<T>::store(vt, 192, ev.w);
+          }
+        }
       } else {
         *(float4*)(a.scratch.open_k[l] + dst) = ks;
         *(float4*)(a.scratch.open_v[l] + dst) = vs;

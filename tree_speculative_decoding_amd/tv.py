@@ -50,7 +50,8 @@ class TvState(ctypes.Structure):
 
 class TvScratch(ctypes.Structure):
     _fields_ = [("entry_k", ctypes.c_void_p * TV_MAX_LEVELS), ("entry_v", ctypes.c_void_p * TV_MAX_LEVELS),
-                ("open_k", ctypes.c_void_p * TV_MAX_LEVELS), ("open_v", ctypes.c_void_p * TV_MAX_LEVELS)]
+                ("open_k", ctypes.c_void_p * TV_MAX_LEVELS), ("open_v", ctypes.c_void_p * TV_MAX_LEVELS),
+                ("in_place", ctypes.c_void_p)]
 
 
 _lib = None
@@ -294,14 +295,18 @@ class DeviceState:
 
 
 class DeviceScratch:
-    """Device tensors of a tv_scratch for B sequences of D nodes."""
+    """Device tensors of a tv_scratch for B sequences of D nodes.  in_place=True gives the
+    struct its in_place mask array (the verify writes one chain's entries straight into the
+    pools and the refresh skips them); False leaves it NULL (every entry is copied)."""
 
-    def __init__(self, B: int, D: int, Hkv: int, d: int, dtype: str, n_levels: int, device="cuda"):
+    def __init__(self, B: int, D: int, Hkv: int, d: int, dtype: str, n_levels: int, device="cuda",
+                 in_place: bool = True):
         td = torch_dtype(dtype)
         self.entry_k = [torch.zeros(B, D, Hkv, d, dtype=td, device=device) for _ in range(n_levels)]
         self.entry_v = [torch.zeros(B, D, Hkv, d, dtype=td, device=device) for _ in range(n_levels)]
         self.open_k = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
         self.open_v = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
+        self.in_place = torch.zeros(B, dtype=torch.int64, device=device) if in_place else None
         self._struct = None
 
     def struct(self) -> TvScratch:
@@ -317,6 +322,7 @@ class DeviceScratch:
             s.entry_v[l] = self.entry_v[l].data_ptr()
             s.open_k[l] = self.open_k[l].data_ptr()
             s.open_v[l] = self.open_v[l].data_ptr()
+        s.in_place = self.in_place.data_ptr() if self.in_place is not None else None
         return s
 
 
