@@ -998,8 +998,8 @@ def time_paged(w, st, stream, reps: int) -> dict:
     for l in range(len(w.levels)):
         pps = st.caps[l] // A
         pages = sp.page_table[l].long().reshape(-1)
-        sp.pool_k[l][pages] = tv.tv.k_to_tiles(st.logical_k(l).reshape(w.B, w.Hkv, pps, A, w.d).permute(0, 2, 1, 3, 4)
-                                               .reshape(w.B * pps, w.Hkv, A, w.d))
+        sp.pool_k[l][pages] = (st.logical_k(l).reshape(w.B, w.Hkv, pps, A, w.d).permute(0, 2, 1, 3, 4)
+                               .reshape(w.B * pps, w.Hkv, A, w.d))
         sp.pool_vt[l][pages] = st.logical_vt(l).permute(0, 2, 1, 3, 4).reshape(w.B * pps, w.Hkv, w.d, A)
         sp.n[l].copy_(st.n[l])
         sp.open_k[l].copy_(st.open_k[l])

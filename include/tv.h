@@ -58,7 +58,7 @@ extern "C" {
 #define TV_API
 #endif
 
-#define TV_VERSION 140      /* 1.4.0: blocked element order inside pool tiles; scratch in_place */
+#define TV_VERSION 130      /* 1.3.0: workspace holds only the partials of split prefixes */
 #define TV_MAX_LEVELS 2
 #define TV_MAX_D 64
 #define TV_TILE_RUN 16     /* tiles of one (sequence, KV head) kept together in a contiguous pool */
@@ -87,11 +87,8 @@ enum {
 
 /* One compression level (the pages' C4 / C128 compressed states, TSD-V4 §2.2, §4.3).
  * A level's entries live in 64-entry tiles (TV_POOL_ALIGN): tile t of (sequence b, KV
- * head g) holds entries 64t .. 64t+63, 64*d elements of K and 64*d of V.  Inside a tile
- * (d a multiple of 32): K element (entry e, channel c) is at ((c/32)*64 + e)*32 + c%32
- * (blocks of 32 channels, entry-major), V element (c, e) at ((e/16)*d + c)*16 + e%16
- * (transposed, blocks of 16 entries), so that every operand the prefix kernel's matrix
- * cores read is one contiguous run of memory.  Contiguous pool (page_table == NULL), T = cap/64 tiles per
+ * head g) holds entries 64t .. 64t+63, as 64 rows of d (K) and as d rows of 64 (V,
+ * transposed inside the tile).  Contiguous pool (page_table == NULL), T = cap/64 tiles per
  * (b, g), R = TV_TILE_RUN: for q < floor(T/R), tiles R*q .. R*q+R-1 of (b, g) are tiles
  * ((q*B + b)*Hkv + g)*R + 0 .. R-1 of k and vt; the last T mod R tiles of (b, g) are tiles
  * floor(T/R)*B*Hkv*R + (b*Hkv + g)*(T mod R) + 0 ..  (k: [B*Hkv*T][64][d] tiles, vt:

@@ -227,7 +227,6 @@ def test_in_place_chain_equals_copy_path(name, fused, paged):
     pool entry -- and the oracle; in_place[b] is the chain of the deepest node (smallest
     index among equals), the whole tree for a single chain."""
     import torch
-    import tree_speculative_decoding_amd as tvmod
     w, T = IN_PLACE[name]
     _say(f"in-place chain {name} fused={fused} paged={paged}: {T} steps")
     caps = pooled_caps(w, T * w.D + 8)
@@ -265,15 +264,21 @@ def test_in_place_chain_equals_copy_path(name, fused, paged):
             assert torch.equal(da.open_k[l], db.open_k[l]) and torch.equal(da.open_v[l], db.open_v[l])
             n = da.n[l].cpu().numpy()
             ka, kb = da.logical_k(l), db.logical_k(l)
-            va = torch.from_numpy(tvmod.tv.untile_vt(tvmod.to_host(da.logical_vt(l).contiguous())).copy())
-            vb = torch.from_numpy(tvmod.tv.untile_vt(tvmod.to_host(db.logical_vt(l).contiguous())).copy())
+            va = tv_untile(da.logical_vt(l))
+            vb = tv_untile(db.logical_vt(l))
             for b in range(w.B):
                 assert torch.equal(_bits(ka[b, :, :n[b]]), _bits(kb[b, :, :n[b]])), f"step {t} level {l} K"
-                assert torch.equal(va[b, :, :n[b]], vb[b, :, :n[b]]), f"step {t} level {l} V"
+                assert torch.equal(_bits(va[b, :, :n[b]]), _bits(vb[b, :, :n[b]])), f"step {t} level {l} V"
         if da.tail_k is not None:
             assert torch.equal(_bits(da.tail_k), _bits(db.tail_k)) and torch.equal(_bits(da.tail_v), _bits(db.tail_v))
         ost = ref.state
     compare_state(db, ost, w.dtype, f"{name} in place, final state")
+
+
+def tv_untile(vt):
+    """[B][Hkv][T][d][64] V tiles -> [B][Hkv][T*64][d] (layout only)."""
+    B, H, T, d, A = vt.shape
+    return vt.transpose(-1, -2).reshape(B, H, T * A, d)
 
 
 FUSED = {

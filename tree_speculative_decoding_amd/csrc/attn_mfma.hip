@@ -198,8 +198,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       for (int x = 0; x < PER; ++x) {
         const int p = tid + x * NT;
         if (kFull || p < 1024) {
-          kpre[x] = load_stream16(kb + (uint32_t)p * 16);  // the tiles are read in memory order
-          vpre[x] = load_stream16(vb + (uint32_t)p * 16);
+          kpre[x] = load_stream16(kb + (uint32_t)p * 16);  // K rows are 256 B: piece p at 16p
+          vpre[x] = load_stream16(vb + (uint32_t)p * 16);  // V^T tile rows are 128 B: piece p at 16p
         }
       }
     };
@@ -209,9 +209,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
         for (int x = 0; x < PER; ++x) {
           const int p = tid + x * NT;
           if (kFull || p < 1024) {
-            const uint32_t krow_ok = ((p >> 2) & 63) < cnt ? 0xffffffffu : 0u;
+            const uint32_t krow_ok = (p >> 4) < cnt ? 0xffffffffu : 0u;
             kpre[x].x &= krow_ok; kpre[x].y &= krow_ok; kpre[x].z &= krow_ok; kpre[x].w &= krow_ok;
-            const int keep = cnt - ((p >> 8) * 16 + (p & 1) * 8);  // committed entries among this piece's 8
+            const int keep = cnt - (p & 7) * 8;  // committed entries among this piece's 8
             vpre[x].x &= (keep > 0 ? 0x0000ffffu : 0u) | (keep > 1 ? 0xffff0000u : 0u);
             vpre[x].y &= (keep > 2 ? 0x0000ffffu : 0u) | (keep > 3 ? 0xffff0000u : 0u);
             vpre[x].z &= (keep > 4 ? 0x0000ffffu : 0u) | (keep > 5 ? 0xffff0000u : 0u);
@@ -223,14 +223,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       for (int x = 0; x < PER; ++x) {
         const int p = tid + x * NT;
         if (kFull || p < 1024) {
-          // K piece p (k_elem order): channels 32(p >> 8) + 8(p & 3) .. +7 of entry (p >> 2) & 63
-          *(uint4*)(Ks + ((p >> 2) & 63) * kKStr + ((p >> 8) * 4 + (p & 3)) * 16) = kpre[x];
-          // V^T piece p (vt_elem order): entries 16(p >> 8) + 8(p & 1) .. +7 of channel
-          // (p >> 1) & 127; its two halves go to their slots in the lane order of the P^T
-          // operand (see v_slot)
-          const int k8 = (p >> 8) * 16 + (p & 1) * 8, ch = (p >> 1) & 127;
-          *(uint2*)(Vs + vt_byte(ch, v_slot(k8))) = make_uint2(vpre[x].x, vpre[x].y);
-          *(uint2*)(Vs + vt_byte(ch, v_slot(k8 + 4))) = make_uint2(vpre[x].z, vpre[x].w);
+          *(uint4*)(Ks + (p >> 4) * kKStr + (p & 15) * 16) = kpre[x];
+          // V^T piece: entries 8k..8k+7 of channel row p/8; its two halves go to their
+          // slots in the lane order of the P^T operand (see v_slot)
+          const int k8 = (p & 7) * 8;
+          *(uint2*)(Vs + vt_byte(p >> 3, v_slot(k8))) = make_uint2(vpre[x].x, vpre[x].y);
+          *(uint2*)(Vs + vt_byte(p >> 3, v_slot(k8 + 4))) = make_uint2(vpre[x].z, vpre[x].w);
         }
       }
     };

@@ -82,11 +82,11 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
         __syncthreads();  // previous tile fully consumed (and Q staged on the first pass)
         for (int e = tid; e < TK * DH; e += 256) {
           const int k = e / DH, dd = e - k * DH;
-          Ks[k][dd] = k < n_sub && page_ok ? Elem<T>::load(pk, tb + k_elem((base + k) & 63, dd)) : 0.f;
+          Ks[k][dd] = k < n_sub && page_ok ? Elem<T>::load(pk, tb + (size_t)((base + k) & 63) * DH + dd) : 0.f;
         }
         for (int e = tid; e < DH * TK; e += 256) {
           const int dd = e / TK, k = e - dd * TK;
-          Vs[dd][k] = k < n_sub && page_ok ? Elem<T>::load(pvt, tb + vt_elem(dd, (base + k) & 63, DH)) : 0.f;
+          Vs[dd][k] = k < n_sub && page_ok ? Elem<T>::load(pvt, tb + (size_t)dd * 64 + ((base + k) & 63)) : 0.f;
         }
         __syncthreads();
         float sc[TK / 4];

@@ -49,8 +49,8 @@ __global__ __launch_bounds__(256) void k_compress_entries(tv_state st, int l, co
   int page;
   if (!tile_page(st.lvl[l], b, j >> 6, &page)) return;  // flagged by k_compress_finish
   const size_t tb = tile_offset(st.lvl[l].page_table != nullptr, page, st.lvl[l].cap, st.B, st.Hkv, d, b, g, j >> 6);
-  Elem<T>::store((T*)st.lvl[l].k, tb + k_elem(j & 63, dd), sk / (float)C);
-  Elem<T>::store((T*)st.lvl[l].vt, tb + vt_elem(dd, j & 63, d), sv / (float)C);
+  Elem<T>::store((T*)st.lvl[l].k, tb + (size_t)(j & 63) * d + dd, sk / (float)C);
+  Elem<T>::store((T*)st.lvl[l].vt, tb + (size_t)dd * 64 + (j & 63), sv / (float)C);
 }
 
 template <typename T>

@@ -171,8 +171,8 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
           const int i = sh.cp[c0 + t], j = sh.it_j[i];
           const tv_level& lv = sh.it_l[i] != 0 ? st.lvl[1] : st.lvl[0];
           const size_t tb = sh.it_tile0[i] + (size_t)g * sh.it_gstep[i];
-          Bits<T>::st((T*)lv.k, tb + k_elem(j & 63, dd), ck[t]);
-          Bits<T>::st((T*)lv.vt, tb + vt_elem(dd, j & 63, d), cv[t]);
+          Bits<T>::st((T*)lv.k, tb + (size_t)(j & 63) * d + dd, ck[t]);
+          Bits<T>::st((T*)lv.vt, tb + (size_t)dd * 64 + (j & 63), cv[t]);
         }
     }
     if (L > 0) {

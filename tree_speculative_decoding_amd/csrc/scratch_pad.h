@@ -211,12 +211,12 @@ __device__ __forceinline__ void scratch_node(const AttnArgs& a, int b, int i, Sc
           if (!paged || (page >= 0 && page < a.npages[l])) {
             const int g = e / a.d, c = e - g * a.d;  // four channels of one head
             const size_t tb = tile_offset(paged, page, a.cap[l], a.B, a.Hkv, a.d, b, g, j >> 6);
-            Quad<T>::store((T*)a.pk[l], tb + k_elem(j & 63, c), ek);  // (c % 4 == 0: one 32-channel block)
-            T* vt = (T*)a.pvt[l] + tb;
-            Elem<T>::store(vt, vt_elem(c, j & 63, a.d), ev.x);
-            Elem<T>::store(vt, vt_elem(c + 1, j & 63, a.d), ev.y);
-            Elem<T>::store(vt, vt_elem(c + 2, j & 63, a.d), ev.z);
-            Elem<T>::store(vt, vt_elem(c + 3, j & 63, a.d), ev.w);
+            Quad<T>::store((T*)a.pk[l], tb + (size_t)(j & 63) * a.d + c, ek);
+            T* vt = (T*)a.pvt[l] + tb + (size_t)c * 64 + (j & 63);
+            Elem<T>::store(vt, 0, ev.x);
+            Elem<T>::store(vt, 64, ev.y);
+            Elem<T>::store(vt, 128, ev.z);
+            Elem<T>::store(vt, 192, ev.w);
           }
         }
       } else {

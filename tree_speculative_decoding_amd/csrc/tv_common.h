@@ -79,15 +79,6 @@ __device__ __forceinline__ size_t tile_offset(bool paged, int page, int cap, int
   return tile * 64 * d;
 }
 
-// Element order inside a pool tile (64 entries x d channels, d a multiple of 32), chosen so
-// that the prefix kernel's matrix-core operands are contiguous runs of memory.  K: blocks of
-// 32 channels, entry-major inside a block ([d/32][64][32]): the 16 entries x 32 channels
-// of one S = K Q^T operand are 1 KB in a row.  V (transposed): blocks of 16 entries,
-// channel-major inside a block ([4][d][16]): the 16 channels x 16 entries of one
-// P V operand are 512 B in a row.  k_elem / vt_elem give the element's index in the tile.
-__device__ __forceinline__ int k_elem(int e, int ch) { return ((ch >> 5) << 11) + (e << 5) + (ch & 31); }
-__device__ __forceinline__ int vt_elem(int ch, int e, int d) { return (((e >> 4) * d + ch) << 4) + (e & 15); }
-
 // Physical page of tile t of sequence b in a level (0 for a contiguous pool); false if the
 // page-table entry is outside [0, num_pages).
 __device__ __forceinline__ bool tile_page(const tv_level& L, int b, int t, int* page) {

@@ -146,56 +146,20 @@ def to_host(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def _swap(x, a: int, b: int):
-    return x.transpose(a, b) if isinstance(x, torch.Tensor) else np.swapaxes(x, a, b)
-
-
-def _contig(x):
-    return x.contiguous() if isinstance(x, torch.Tensor) else np.ascontiguousarray(x)
-
-
-# Element order inside a pool tile (include/tv.h): K tiles [64 entries][d] are stored in
-# blocks of 32 channels ([d/32][64][32]); V tiles, transposed [d][64 entries], in blocks of
-# 16 entries ([4][d][16]).  These convert the last two axes of tensors of tiles between
-# the plain order and the stored one (numpy arrays or torch tensors; layout only).
-def k_to_tiles(x):
-    """[..., 64, d] entry-major K tiles -> stored order (same shape)."""
-    *lead, a, d = x.shape
-    return _contig(_swap(x.reshape(*lead, a, d // 32, 32), -3, -2)).reshape(*lead, a, d)
-
-
-def k_from_tiles(x):
-    """Inverse of k_to_tiles."""
-    *lead, a, d = x.shape
-    return _contig(_swap(x.reshape(*lead, d // 32, a, 32), -3, -2)).reshape(*lead, a, d)
-
-
-def vt_to_tiles(x):
-    """[..., d, 64] transposed V tiles -> stored order (same shape)."""
-    *lead, d, a = x.shape
-    return _contig(_swap(x.reshape(*lead, d, a // 16, 16), -3, -2)).reshape(*lead, d, a)
-
-
-def vt_from_tiles(x):
-    """Inverse of vt_to_tiles."""
-    *lead, d, a = x.shape
-    return _contig(_swap(x.reshape(*lead, a // 16, d, 16), -3, -2)).reshape(*lead, d, a)
-
-
 def tile_vt(v: np.ndarray, cap: int) -> np.ndarray:
-    """Entry-major V rows [..., n, d] -> the pool's V tiles [..., cap/64, d, 64] in stored
-    order (entries n..cap-1 zero).  Layout conversion only."""
+    """Entry-major V rows [..., n, d] -> the pool's tiled transposed layout [..., cap/64, d, 64]
+    (entries n..cap-1 zero).  Layout conversion only."""
     *lead, n, d = v.shape
     full = np.zeros((*lead, cap, d), dtype=v.dtype)
     full[..., :n, :] = v
     t = full.reshape(*lead, cap // TV_POOL_ALIGN, TV_POOL_ALIGN, d)
-    return vt_to_tiles(np.ascontiguousarray(np.swapaxes(t, -1, -2)))
+    return np.ascontiguousarray(np.swapaxes(t, -1, -2))
 
 
 def untile_vt(vt: np.ndarray) -> np.ndarray:
-    """Inverse of tile_vt: stored V tiles [..., cap/64, d, 64] -> [..., cap, d]."""
+    """Inverse of tile_vt: [..., cap/64, d, 64] -> [..., cap, d]."""
     *lead, nt, d, w = vt.shape
-    return np.swapaxes(vt_from_tiles(vt), -1, -2).reshape(*lead, nt * w, d)
+    return np.swapaxes(vt, -1, -2).reshape(*lead, nt * w, d)
 
 
 def round_cap(n: int) -> int:
@@ -301,32 +265,28 @@ class DeviceState:
             idx = self.tile_index[l][b]  # [Hkv][cap/64]
             full, r = n // A, n % A
             if full:
-                self.pool_k[l][idx[:, :full].reshape(-1)] = k_to_tiles(k[:, :full * A].reshape(self.Hkv * full, A, self.d))
-            if r:  # the last, partial tile: its entries past n keep their contents
-                last = k_from_tiles(self.pool_k[l][idx[:, full]])
-                last[:, :r] = k[:, full * A:n]
-                self.pool_k[l][idx[:, full]] = k_to_tiles(last)
+                self.pool_k[l][idx[:, :full].reshape(-1)] = k[:, :full * A].reshape(self.Hkv * full, A, self.d)
+            if r:
+                self.pool_k[l][idx[:, full], :r] = k[:, full * A:n]
             self.pool_vt[l][idx.reshape(-1)] = vt.reshape(-1, self.d, A)
             return
         pps = self.caps[l] // A
         pages = self.page_table[l][b].long()
         kk = torch.zeros(self.Hkv, self.caps[l], self.d, dtype=k.dtype, device=k.device)
         kk[:, :n] = k
-        self.pool_k[l][pages] = k_to_tiles(kk.reshape(self.Hkv, pps, A, self.d).permute(1, 0, 2, 3))
+        self.pool_k[l][pages] = kk.reshape(self.Hkv, pps, A, self.d).permute(1, 0, 2, 3)
         self.pool_vt[l][pages] = vt.permute(1, 0, 2, 3)
 
     def logical_k(self, l: int) -> torch.Tensor:
-        """Level l's K pool as [B][Hkv][cap][d], entries in order (a gather)."""
+        """Level l's K pool as [B][Hkv][cap][d] (a gather)."""
         if not self.paged:
-            return k_from_tiles(self.pool_k[l][self.tile_index[l].reshape(-1)]).reshape(
-                self.B, self.Hkv, self.caps[l], self.d)
+            return self.pool_k[l][self.tile_index[l].reshape(-1)].reshape(self.B, self.Hkv, self.caps[l], self.d)
         A = TV_POOL_ALIGN
-        g = k_from_tiles(self.pool_k[l][self.page_table[l].long()])  # [B][pps][Hkv][64][d]
+        g = self.pool_k[l][self.page_table[l].long()]  # [B][pps][Hkv][64][d]
         return g.permute(0, 2, 1, 3, 4).reshape(self.B, self.Hkv, self.caps[l], self.d)
 
     def logical_vt(self, l: int) -> torch.Tensor:
-        """Level l's V tiles as [B][Hkv][cap/64][d][64] in stored order (a gather; untile_vt
-        turns them into entries)."""
+        """Level l's V tiles as [B][Hkv][cap/64][d][64] (a gather)."""
         if not self.paged:
             T = self.caps[l] // TV_POOL_ALIGN
             return self.pool_vt[l][self.tile_index[l].reshape(-1)].reshape(self.B, self.Hkv, T, self.d, TV_POOL_ALIGN)
