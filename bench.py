@@ -148,6 +148,21 @@ def _headline_steps(trace_csv: str, n_steps: int) -> list:
     return steps
 
 
+def _counter_per_kernel(path: str, counter: str) -> dict:
+    """Mean value of a counter per dispatch (FETCH_SIZE / WRITE_SIZE: KiB; the derived
+    utilisation metrics: percent or a ratio), by kernel name, from a rocprofv3 csv."""
+    import csv
+    acc = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            v = acc.setdefault(r["Kernel_Name"], [0.0, 0])
+            v[0] += float(r["Counter_Value"])
+            v[1] += 1
+    return {k: v[0] / v[1] for k, v in acc.items()}
+
+
 def summarize_profiles(d: str, workload: str) -> None:
     """Turn the rocprofv3 csv runs of the profiling commands below into the committed
     summaries: every launch of the headline's steps in order (warm-up and timed), the
