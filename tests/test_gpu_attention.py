@@ -199,7 +199,7 @@ def test_other_branches_never_read():
 EDGE = {
     # bf16, head dim 64 -> vector kernel
     "bf16_d64": synth.Workload("e1", 3, 7, 8, 2, 64, "bf16", (4, 128), 384, 2, 3, 0.6, 2001),
-    # 128 query rows per KV head -> two 64-row blocks
+    # 128 query rows per KV head -> one 128-row unit (8-wave workgroups)
     "two_row_blocks": synth.Workload("e2", 2, 8, 32, 2, 128, "bf16", (4, 128), 640, 2, 3, 0.6, 2002),
     # a single node (no drafts)
     "root_only": synth.Workload("e3", 3, 1, 16, 2, 128, "bf16", (4, 128), 256, 1, 0, 0.6, 2003),
@@ -215,8 +215,12 @@ EDGE = {
     "deep_chain": synth.Workload("e8", 1, 64, 8, 1, 128, "bf16", (4,), 100, 1, 63, 0.9, 2008, prefix="raw"),
     # tail + tree = 2 + 24 entries: two 16-entry tiles in the prefix kernel's tree chunk
     "tree_two_tiles": synth.Workload("e9", 2, 24, 16, 2, 128, "bf16", (4, 128), 1502, 3, 5, 0.6, 2009, prefix="raw"),
-    # tail + tree = 3 + 61 = 64 entries: the largest tree chunk, 6 row blocks
+    # tail + tree = 3 + 61 = 64 entries: the largest tree chunk, 4 blocks of 128 rows
     "tree_full_chunk": synth.Workload("e10", 1, 61, 8, 1, 128, "bf16", (4, 128), 1203, 4, 5, 0.6, 2010, prefix="raw"),
+    # 64 rows per KV head (G = 2, D = 32) with a 35-entry tail + tree chunk: four 16-entry
+    # tiles in a 4-wave, 64-row unit
+    "tree_four_tiles_64rows": synth.Workload("e11", 2, 32, 4, 2, 128, "bf16", (4, 128), 1501, 2, 5, 0.6, 2011,
+                                             prefix="raw"),
 }
 
 

@@ -3,11 +3,11 @@
 // merge the prefix-stream partials of a query row, add the finest level's raw tail and
 // the node's own chain, and normalise.
 //
-// One workgroup of 4 waves per (sequence, KV head, 16 rows of a 64-row block), one wave
-// per query row r = node * G + head-in-group, each lane d/64 channels of the row.  The
+// One workgroup of 4 waves per (sequence, KV head, 4 rows of a unit's block of
+// unit_rows = 64 or 128 query rows), one wave per query row r = node * G + head-in-group, each lane d/64 channels of the row.  The
 // partials of a row are merged across lanes, not one after another: the lanes read the
 // slices' (max, sum) pairs together and reduce the common maximum M, then the partial
-// rows are read eight at a time with no load waiting on another and summed with weights
+// rows are read 16 at a time with no load waiting on another and summed with weights
 // 2^(m_s - M) (slices with an empty sum weigh nothing, by selection).  For the paths
 // whose prefix kernel does not attend the tail and the chain, the D tree tokens of the
 // KV head are staged in LDS, and the chain is the node's ancestor mask: only its set

@@ -4,10 +4,12 @@
 // history), §2.1 / §5.3 (verification of many candidates is memory-bound at small
 // batch: the prefix is read once for all G*D query rows of a KV head).
 //
-// A unit is one (sequence, KV head, 64-row block); the units' prefixes, cut into
-// 64-entry chunks and laid end to end, are split into equal slices, one persistent
-// workgroup each (one round on the GPU).  NW waves per workgroup, 16 query rows per
-// wave (rows r = node * G + head-in-group).  Per 64-entry chunk:
+// A unit is one (sequence, KV head, block of 16 * NW query rows): 64-row units in 4-wave
+// workgroups (two per CU), or, when a KV head has more than 64 rows (G * D > 64),
+// 128-row units in 8-wave workgroups (one per CU) so that every row of the head shares
+// one stream.  The units' prefixes, cut into 64-entry chunks and laid end to end, are
+// split into equal slices, one persistent workgroup each (one round on the GPU); 16
+// query rows per wave (rows r = node * G + head-in-group).  Per 64-entry chunk:
 //   1. the K chunk (64 x 128, row-major) and the V^T tile (128 x 64; the V pool is
 //      stored transposed per 64-entry tile) are each one contiguous 16 KB block,
 //      loaded with 16-byte coalesced loads into registers two chunks ahead (two
@@ -526,8 +528,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
-  // Always four waves: all of them load (32 KB per chunk), waves whose 16 rows are all
-  // past the G*D query rows skip the arithmetic.  One workgroup per slice.
+  // NW waves per workgroup (4 for 64-row units, 8 for 128-row units): all of them load
+  // (32 KB per chunk), waves whose 16 rows are all past the G*D query rows skip the
+  // arithmetic.  One workgroup per slice.
   if (a.parts == 0) return hipSuccess;
   const int tt = a.fused_tree ? a.tree_tiles : 1;
   const bool paged = a.pt[0] != nullptr;  // every level or none
