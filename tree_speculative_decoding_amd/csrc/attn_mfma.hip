@@ -243,16 +243,25 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
     // Attend to the chunk in LDS.  hide(t, i) is true for the scores to leave out (entry
     // 16t + 4grp + i of this lane's row); it is only evaluated when `masked`.
     auto attend = [&](bool masked, auto hide) {
-      // S^T tiles: sacc[t] lane (n16, grp) = S[row n16][entry 16t + 4grp + i]
+      // S^T tiles: sacc[t] lane (n16, grp) = S[row n16][entry 16t + 4grp + i].  The K
+      // operands of tile t + 1 are read from LDS into a second set of registers before
+      // tile t's products, which lets the compiler keep several reads in flight (each wait
+      // covers only the older reads) instead of waiting for every read before its product:
+      // the LDS latency then overlaps the matrix cores instead of adding up read by read.
       f32x4 sacc[4];
+      bf16x8 kop[2][4];
+      auto read_k = [&](int t, bf16x8 (&dst)[4]) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) dst[ks] = *(const bf16x8*)(Ks + (16 * t + n16) * kKStr + (32 * ks + 8 * grp) * 2);
+      };
+      read_k(0, kop[0]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
+        if (t < 3) read_k(t + 1, kop[(t + 1) & 1]);
         sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 kop = *(const bf16x8*)(Ks + (16 * t + n16) * kKStr + (32 * ks + 8 * grp) * 2);
-          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[ks], sacc[t], 0, 0, 0);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[t & 1][ks], qop[ks], sacc[t], 0, 0, 0);
       }
       // Online softmax in base-2 units.  The scale is applied inside the exponent (one
       // fma per score); the row max is taken on raw scores (scale > 0).
@@ -293,12 +302,22 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       }
       // O^T += V^T P^T; k-step h: slots 32h + 8grp .. +7 hold entries 32h + 4grp + {0..3}
       // and 32h + 16 + 4grp + {0..3}
+      // (the V^T operands of channel tiles 2j + 2, 2j + 3 are read into a second set of
+      // registers before those of 2j, 2j + 1 are used, as for K)
+      bf16x8 vop[2][4];
+      auto read_v = [&](int j, bf16x8 (&dst)[4]) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
+        for (int x = 0; x < 4; ++x)
+          dst[x] = *(const bf16x8*)(Vs + vt_byte(16 * (2 * j + (x >> 1)) + n16, 32 * (x & 1) + 8 * grp));
+      };
+      read_v(0, vop[0]);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const bf16x8 vop = *(const bf16x8*)(Vs + vt_byte(16 * dt + n16, 32 * h + 8 * grp));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[h], oacc[dt], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        if (j < 3) read_v(j + 1, vop[(j + 1) & 1]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int dt = 2 * j + (x >> 1);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[j & 1][x], pop[x & 1], oacc[dt], 0, 0, 0);
         }
       }
     };
