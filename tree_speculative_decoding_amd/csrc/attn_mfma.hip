@@ -196,12 +196,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
           vb = (const char*)a.pvt[lvl] + off;  // V^T tile
         }
       }
+      // piece p = tid + x * NT at byte 16p of each tile (K rows are 256 B, V^T rows 128 B):
+      // a uniform base per x plus the thread's own 32-bit offset
 #pragma unroll
       for (int x = 0; x < PER; ++x) {
         const int p = tid + x * NT;
         if (kFull || p < 1024) {
-          kpre[x] = load_stream16(kb + (uint32_t)p * 16);  // K rows are 256 B: piece p at 16p
-          vpre[x] = load_stream16(vb + (uint32_t)p * 16);  // V^T tile rows are 128 B: piece p at 16p
+          kpre[x] = load_stream16(kb + x * NT * 16 + (uint32_t)tid * 16);
+          vpre[x] = load_stream16(vb + x * NT * 16 + (uint32_t)tid * 16);
         }
       }
     };
@@ -221,16 +223,21 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
           }
         }
       }
+      // piece p = tid + x * NT: K row p / 16, 16-byte unit p % 16; V^T channel row p / 8,
+      // entries 8 (p % 8) .. +7, whose two halves go to their slots in the lane order of the
+      // P^T operand (see v_slot).  NT is a multiple of 128, so the LDS address of piece x is
+      // thread tid's address plus a constant (row r + NT/8 has the swizzle of row r), which
+      // the stores carry as an immediate offset instead of a register per piece.
+      char* k_st = Ks + (tid >> 4) * kKStr + (tid & 15) * 16;
+      char* v_st0 = Vs + vt_byte(tid >> 3, v_slot((tid & 7) * 8));
+      char* v_st1 = Vs + vt_byte(tid >> 3, v_slot((tid & 7) * 8 + 4));
 #pragma unroll
       for (int x = 0; x < PER; ++x) {
         const int p = tid + x * NT;
         if (kFull || p < 1024) {
-          *(uint4*)(Ks + (p >> 4) * kKStr + (p & 15) * 16) = kpre[x];
-          // V^T piece: entries 8k..8k+7 of channel row p/8; its two halves go to their
-          // slots in the lane order of the P^T operand (see v_slot)
-          const int k8 = (p & 7) * 8;
-          *(uint2*)(Vs + vt_byte(p >> 3, v_slot(k8))) = make_uint2(vpre[x].x, vpre[x].y);
-          *(uint2*)(Vs + vt_byte(p >> 3, v_slot(k8 + 4))) = make_uint2(vpre[x].z, vpre[x].w);
+          *(uint4*)(k_st + x * (NT / 16) * kKStr) = kpre[x];
+          *(uint2*)(v_st0 + x * (NT / 8) * kVStr) = make_uint2(vpre[x].x, vpre[x].y);
+          *(uint2*)(v_st1 + x * (NT / 8) * kVStr) = make_uint2(vpre[x].z, vpre[x].w);
         }
       }
     };
