@@ -184,16 +184,32 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
     // committed count are zeroed by selection when the chunk is written to LDS.
     // Slots c >= c_hi (past the unit's stream) read the zero block, and so does a chunk of a
     // paged pool whose page id is out of range.  `pid` is the chunk's page (paged pools).
+    // Contiguous pools: tile_offset's placement with its per-unit parts worked out once, so
+    // that a chunk's tile costs a compare, a shift and a multiply-add (scalar) rather than
+    // the full computation: tile t of level l (t < 16 * full_l) is run0 + (t / 16) * run_step
+    // + t % 16, a tile of the last incomplete run is tail0_l + t - 16 * full_l.
+    const int bgi = b * a.Hkv + g;
+    const int run_step = a.B * a.Hkv * kTileRun;
+    const int full0 = a.cap[0] / 64 / kTileRun, full1 = a.n_levels > 1 ? a.cap[1] / 64 / kTileRun : 0;
+    const int tail00 = full0 * run_step + bgi * (a.cap[0] / 64 - full0 * kTileRun);
+    const int tail01 = a.n_levels > 1 ? full1 * run_step + bgi * (a.cap[1] / 64 - full1 * kTileRun) : 0;
     auto load_chunk = [&](int c, int pid, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
       const char* kb = (const char*)g_zero_chunk;
       const char* vb = kb;
       if (c < c_hi) {  // uniform
-        int lvl, e0, cnt;
-        chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
-        if (!PAGED || (pid >= 0 && pid < (lvl == 0 ? a.npages[0] : a.npages[1]))) {
-          const size_t off = tile_offset(PAGED, pid, a.cap[lvl], a.B, a.Hkv, kDH, b, g, e0 >> 6) * 2;
-          kb = (const char*)a.pk[lvl] + off;   // K rows
-          vb = (const char*)a.pvt[lvl] + off;  // V^T tile
+        const bool l1 = c >= T0;
+        const int t = l1 ? c - T0 : c;  // the chunk's tile within its level
+        if (!PAGED) {
+          const int full = l1 ? full1 : full0;
+          const int tile = t < full * kTileRun ? bgi * kTileRun + (t / kTileRun) * run_step + t % kTileRun
+                                               : (l1 ? tail01 : tail00) + t - full * kTileRun;
+          const size_t off = (size_t)tile * (64 * kDH * 2);
+          kb = (const char*)(l1 ? a.pk[1] : a.pk[0]) + off;    // K rows
+          vb = (const char*)(l1 ? a.pvt[1] : a.pvt[0]) + off;  // V^T tile
+        } else if (pid >= 0 && pid < (l1 ? a.npages[1] : a.npages[0])) {
+          const size_t off = tile_offset(true, pid, 0, a.B, a.Hkv, kDH, b, g, t) * 2;
+          kb = (const char*)(l1 ? a.pk[1] : a.pk[0]) + off;
+          vb = (const char*)(l1 ? a.pvt[1] : a.pvt[0]) + off;
         }
       }
       // piece p = tid + x * NT at byte 16p of each tile (K rows are 256 B, V^T rows 128 B):
