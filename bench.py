@@ -98,8 +98,15 @@ class TimingEvent:
         return float(ms.value)
 
     def __del__(self):
-        if TimingEvent._hip is not None and self.handle:
-            TimingEvent._hip.hipEventDestroy(self._ct.c_void_p(self.handle))
+        # (at interpreter exit the module's globals may already be gone: reach the runtime
+        # through the instance's class and give up quietly)
+        hip = getattr(type(self), "_hip", None)
+        handle = getattr(self, "handle", None)
+        if hip is not None and handle:
+            try:
+                hip.hipEventDestroy(self._ct.c_void_p(handle))
+            except Exception:
+                pass
 
 
 def calibrate_copy(mib: int):
