@@ -124,6 +124,28 @@ def calibrate_copy(mib: int):
 
 PROFILE_BENCH = "python3 bench.py --gpus 1 --steps 20 --warmup 5"  # the headline command itself
 PROFILE_COUNTER_BENCH = "python3 bench.py --gpus 1 --steps 20 --warmup 5 --no-cpu-baseline --no-extras"
+
+
+def profile_cmd(workload: str, counters: bool) -> str:
+    """The bench command a profile of `workload` runs: the headline command itself for the
+    headline's kernel trace, else the same steps without the CPU baseline and the extras."""
+    if workload == "high_batch":
+        return PROFILE_COUNTER_BENCH if counters else PROFILE_BENCH
+    return PROFILE_COUNTER_BENCH + f" --workload {workload}"
+
+
+def find_workload(name: str):
+    """A named workload, or a point of the long-context sweep by its name."""
+    import synth
+    if name in synth.WORKLOADS:
+        return synth.WORKLOADS[name]
+    for w in synth.sweep_workloads():
+        if w.name == name:
+            return w
+    raise SystemExit(f"unknown workload {name!r}: one of {sorted(synth.WORKLOADS)} or a sweep point name "
+                     "(sweep_s<steps>_k<topk>_d<D>_b<B>_p<p>)")
+
+
 PREFIX_KERNEL = "tv::k_attn_mfma<4, 1, false>"  # the contiguous-pool instance the benchmark runs
 STEP_KERNELS = ("k_tree_mask", "k_scratch", "k_attn_mfma", "k_attn_finish", "k_accept", "k_refresh")
 CALL_KERNELS = ("k_scratch", "k_attn_mfma", "k_attn_finish")  # what one tv_verify_attn call launches
@@ -181,15 +203,15 @@ def summarize_profiles(d: str, workload: str) -> None:
     bench_line = [l for l in open(os.path.join(d, "kt.txt")).read().splitlines() if l.startswith("{")][-1]
     bl = json.loads(bench_line)
     W, K = bl["warmup"], bl["steps"]
-    kt_cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {PROFILE_BENCH}"
+    kt_cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- {profile_cmd(workload, False)}"
     steps = _headline_steps(os.path.join(d, "kt", "run_kernel_trace.csv"), W + K)
     alg = bl["roofline"]["algorithmic_bytes_per_launch"]
     cfg = bl["config"]
-    lines = [f"# Kernel trace of the headline command: the verify step at {workload} "
+    lines = [f"# Kernel trace of the bench command: the verify step at {workload} "
              f"(B={cfg['B']}, D={cfg['D']}, {cfg['Hq']}/{cfg['Hkv']} heads, d={cfg['head_dim']}, {bl['dtype']}, "
              f"{cfg['prefix_tokens']}-token prefix)", "",
              "Command (from the repository root, TMPDIR=/tmp):", "", "    " + kt_cmd, "",
-             f"Every launch of the headline's {W} untimed and {K} timed steps, in order (`run_kernel_trace.csv`), in us.",
+             f"Every launch of the run's {W} untimed and {K} timed steps, in order (`run_kernel_trace.csv`), in us.",
              "`call` is the tv_verify_attn call on the GPU: from the start of its first kernel to the end of its last;",
              "`step` from the step's first kernel start to its last kernel end.", "",
              "| step | " + " | ".join(k.replace("k_", "") for k in STEP_KERNELS) + " | call | step |",
@@ -232,7 +254,7 @@ def summarize_profiles(d: str, workload: str) -> None:
     # algorithmic bytes of the counter runs themselves
     fl = json.loads([l for l in open(os.path.join(d, "FETCH_SIZE.txt")).read().splitlines() if l.startswith("{")][-1])
     alg_c = fl["roofline"]["algorithmic_bytes_per_launch"]
-    cmd = f"rocprofv3 --pmc {{}} --output-format csv -d <dir> -o run -- {PROFILE_COUNTER_BENCH}"
+    cmd = f"rocprofv3 --pmc {{}} --output-format csv -d <dir> -o run -- {profile_cmd(workload, True)}"
     rec = {"kernels": [_short(k) for k in in_call], "workload": workload,
            "command_fetch": cmd.format("FETCH_SIZE"), "command_write": cmd.format("WRITE_SIZE"),
            "command_calibration": "rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE --output-format csv -d <dir> -o run -- "
@@ -278,7 +300,7 @@ def summarize_utilisation(path: str, workload: str, bench_line: dict) -> None:
     (rocprofv3's own definitions): MFMA busy cycles per SIMD, VALU busy, LDS busy and LDS
     bank conflicts per access, per kernel, as the committed summary."""
     vals = {m: _counter_per_kernel(path, m) for m in UTIL_METRICS}
-    cmd = f"rocprofv3 --pmc {' '.join(UTIL_METRICS)} --output-format csv -d <dir> -o run -- {PROFILE_COUNTER_BENCH}"
+    cmd = f"rocprofv3 --pmc {' '.join(UTIL_METRICS)} --output-format csv -d <dir> -o run -- {profile_cmd(workload, True)}"
     kernels = sorted({k for v in vals.values() for k in v if "tv::" in k})
     lines = [f"# Compute-side counters per dispatch: the verify step at {workload}", "",
              "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmd, "",
@@ -295,8 +317,8 @@ def summarize_utilisation(path: str, workload: str, bench_line: dict) -> None:
         (bench_line["config"]["B"] * bench_line["config"]["Hkv"] * bench_line["config"]["head_dim"] * 4.0)
     lines += ["", f"Algorithmic MFMA work of the prefix kernel at this shape: about {flops / 1e12:.3f} TFLOP per launch "
               f"(4 * B * Hq * D * d per committed entry), {flops / (bench_line['roofline']['avg_call_ms'] * 1e-3) / 1e12:.0f} "
-              "TFLOP/s at the launch time of the same run, against 2500 TFLOP/s dense bf16: the kernel is bound by HBM, "
-              "and the matrix cores are busy for the share of cycles shown.", ""]
+              "TFLOP/s at the call time of the same run, against 2500 TFLOP/s dense bf16: the matrix cores are busy "
+              "for the share of cycles shown.", ""]
     open(os.path.join(ROOT, "profiles", f"utilisation_{workload}.md"), "w").write("\n".join(lines))
 
 
@@ -551,7 +573,7 @@ def main():
     import synth
     import tree_speculative_decoding_amd as tv
 
-    w = synth.WORKLOADS[args.workload]
+    w = find_workload(args.workload)
     torch.cuda.set_device(0)
     B, D = w.B, w.D
     total_steps = args.warmup + args.steps
