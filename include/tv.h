@@ -93,7 +93,9 @@ enum {
  * ((q*B + b)*Hkv + g)*R + 0 .. R-1 of k and vt; the last T mod R tiles of (b, g) are tiles
  * floor(T/R)*B*Hkv*R + (b*Hkv + g)*(T mod R) + 0 ..  (k: [B*Hkv*T][64][d] tiles, vt:
  * [B*Hkv*T][d][64]).  A step reads every sequence's prefix at once; this keeps those reads
- * within one window of memory instead of at a fixed stride of one sequence's pool.
+ * within one window of memory instead of at a fixed stride of one sequence's pool.  The
+ * addresses depend on B, so a contiguous pool serves a fixed number of sequence slots; a
+ * batch that grows and shrinks uses the paged form.
  * Paged pool (TSD-V4 §4.2: a page-based pool whose pages are referenced by pointers):
  * k and vt hold num_pages physical pages, each
  * the tiles of all Hkv heads for 64 entries ([num_pages][Hkv][64][d] and
