@@ -14,7 +14,9 @@
 //      stored transposed per 64-entry tile) are each one contiguous 16 KB block,
 //      loaded with 16-byte coalesced loads into registers two chunks ahead (two
 //      register buffers), all issued back to back, then written to LDS (straight
-//      copies, padded rows);
+//      copies, padded rows), into one of two LDS buffers by chunk parity, so that a
+//      chunk costs one barrier: the buffer written for chunk c was last read for chunk
+//      c - 2, which every wave finished before the barrier after chunk c - 1's stores;
 //   2. S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the K chunk is the A operand
 //      (16 entries x 32 channels per lane group), Q^T the B operand kept in
 //      registers; the accumulator gives each lane one query row and 4 entries per
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
   static_assert(TT >= 1 && TT <= 4, "the tail + tree chunk is at most 64 entries");
   constexpr int TPER = (TT * 256 + NT - 1) / NT;  // its K (and V) pieces per thread
   constexpr bool kTFull = (TT * 256) % NT == 0;
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[2 * kLdsBytes];  // two chunk buffers (two workgroups fit a CU)
   __shared__ uint64_t anc_s[TV_MAX_D];
   char* Ks = smem;
   char* Vs = smem + kChunk * kKStr;
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
         }
       }
     };
-    auto store_chunk = [&](int cnt, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
+    auto store_chunk = [&](int cnt, uint4 (&kpre)[PER], uint4 (&vpre)[PER], int buf) {
       if (cnt < 64) {  // partial chunk (uniform): zero what lies past the committed count
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
@@ -244,9 +246,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       // P^T operand (see v_slot).  NT is a multiple of 128, so the LDS address of piece x is
       // thread tid's address plus a constant (row r + NT/8 has the swizzle of row r), which
       // the stores carry as an immediate offset instead of a register per piece.
-      char* k_st = Ks + (tid >> 4) * kKStr + (tid & 15) * 16;
-      char* v_st0 = Vs + vt_byte(tid >> 3, v_slot((tid & 7) * 8));
-      char* v_st1 = Vs + vt_byte(tid >> 3, v_slot((tid & 7) * 8 + 4));
+      char* k_st = Ks + buf * kLdsBytes + (tid >> 4) * kKStr + (tid & 15) * 16;
+      char* v_st0 = Vs + buf * kLdsBytes + vt_byte(tid >> 3, v_slot((tid & 7) * 8));
+      char* v_st1 = Vs + buf * kLdsBytes + vt_byte(tid >> 3, v_slot((tid & 7) * 8 + 4));
 #pragma unroll
       for (int x = 0; x < PER; ++x) {
         const int p = tid + x * NT;
@@ -265,7 +267,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
 
     // Attend to the chunk in LDS.  hide(t, i) is true for the scores to leave out (entry
     // 16t + 4grp + i of this lane's row); it is only evaluated when `masked`.
-    auto attend = [&](bool masked, auto hide) {
+    auto attend = [&](bool masked, auto hide, int buf) {
+      const char* Kb = Ks + buf * kLdsBytes;
+      const char* Vb = Vs + buf * kLdsBytes;
       // S^T tiles: sacc[t] lane (n16, grp) = S[row n16][entry 16t + 4grp + i].  The K
       // operands of tile t + 1 are read from LDS into a second set of registers before
       // tile t's products, which lets the compiler keep several reads in flight (each wait
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       bf16x8 kop[2][4];
       auto read_k = [&](int t, bf16x8 (&dst)[4]) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) dst[ks] = *(const bf16x8*)(Ks + (16 * t + n16) * kKStr + (32 * ks + 8 * grp) * 2);
+        for (int ks = 0; ks < 4; ++ks) dst[ks] = *(const bf16x8*)(Kb + (16 * t + n16) * kKStr + (32 * ks + 8 * grp) * 2);
       };
       read_k(0, kop[0]);
 #pragma unroll
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       auto read_v = [&](int j, bf16x8 (&dst)[4]) {
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          dst[x] = *(const bf16x8*)(Vs + vt_byte(16 * (2 * j + (x >> 1)) + n16, 32 * (x & 1) + 8 * grp));
+          dst[x] = *(const bf16x8*)(Vb + vt_byte(16 * (2 * j + (x >> 1)) + n16, 32 * (x & 1) + 8 * grp));
       };
       read_v(0, vop[0]);
 #pragma unroll
@@ -364,21 +368,22 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
     // One prefix chunk slot: if c is in the stream, write its chunk to LDS; refill the
     // slot's registers with chunk c + 2 (always issued, so that it is in flight with
     // chunk c + 1's loads); attend.
-    auto step = [&](int c, uint4 (&kpre)[PER], uint4 (&vpre)[PER]) {
+    auto step = [&](int c, uint4 (&kpre)[PER], uint4 (&vpre)[PER], int buf) {
       const bool have = c < c_hi;  // uniform
       int cnt = 0;
       if (have) {
         int lvl, e0;
         chunk_entries(n0, T0, n1, c, &lvl, &e0, &cnt);
-        __syncthreads();  // every wave is done reading the previous chunk
-        store_chunk(cnt, kpre, vpre);
+        // (LDS buffer buf was last read for chunk c - 2: every wave finished that before
+        // the barrier that followed chunk c - 1's stores)
+        store_chunk(cnt, kpre, vpre, buf);
         __syncthreads();
       }
       const int pid = pid_next;
       pid_next = load_pid(c + 3);
       load_chunk(c + 2, pid, kpre, vpre);
       if (!have || !wave_has_rows) return;
-      attend(cnt < 64, [&](int t, int i) { return 16 * t + 4 * grp + i >= cnt; });
+      attend(cnt < 64, [&](int t, int i) { return 16 * t + 4 * grp + i >= cnt; }, buf);
     };
 
     // The unit's tail + chain chunk, attended first: entries [0, rr) are the finest level's
@@ -529,9 +534,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       }
     }
 
+    __syncthreads();  // every wave is done with the tree chunk's LDS and the previous unit's
     for (int c = c_lo; c < c_hi; c += 2) {
-      step(c, kpa, vpa);
-      step(c + 1, kpb, vpb);
+      step(c, kpa, vpa, 0);
+      step(c + 1, kpb, vpb, 1);
     }
 
     l_run += __shfl_xor(l_run, 16, 64);
