@@ -19,10 +19,11 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def run_verify(w, step=0, q_scale=1.0, num_parts=0, poison=True, mutate=None):
-    """Run plan + verify on the GPU and in the oracle for workload w; returns both sides."""
+def run_verify(w, step=0, q_scale=1.0, num_parts=0, poison=True, mutate=None, extra_tokens=64):
+    """Run plan + verify on the GPU and in the oracle for workload w (pools sized for
+    extra_tokens past the prefix); returns both sides."""
     import torch
-    caps = pooled_caps(w, 64)
+    caps = pooled_caps(w, extra_tokens)
     dst = device_state(w, caps, poison=poison)
     ost = oracle_state(w, caps)
     s = synth.step_inputs(w, step, q_scale=q_scale)
@@ -122,6 +123,19 @@ def test_partition_invariance(name, parts):
     res = run_verify(w, num_parts=parts)
     check_outputs(res)
     check_scratch(res)
+
+
+@pytest.mark.parametrize("name,parts", [("linear", 100), ("tree", 100), ("linear", 0), ("tree", 0)])
+def test_pool_headroom(name, parts):
+    """The same committed history in pools with about 4x headroom: three quarters of the
+    capacity slots the slices are cut over hold no committed entry (whole slices of
+    them, for the later workgroups); the rows and the scratch pad still match the oracle."""
+    _say(f"headroom {name} parts={parts}")
+    w = synth.WORKLOADS[name]
+    b = run_verify(w, num_parts=parts, extra_tokens=3 * w.P + 64)
+    assert b["dst"].caps[0] >= 3 * (w.P // w.levels[0]), b["dst"].caps
+    check_outputs(b)
+    check_scratch(b)
 
 
 def test_scratch_pad_paths_bit_identical():
