@@ -70,11 +70,16 @@ __device__ __forceinline__ int vt_byte(int r, int s) {
 // (v_permlane16_swap / v_permlane32_swap, vector ALU) return the two 16-lane (32-lane)
 // halves of each pair, so the larger of the two results is the pair's maximum in every
 // lane -- no trip through the LDS crossbar as for a general shuffle.
+// Maximum of two scores as v_maximum3_f32 (NaN-propagating): fmaxf's IEEE maxNum makes the
+// compiler quiet each matrix-core result first (one more instruction per score).  A NaN
+// score would poison its row either way (its exp2 is NaN); excluded entries are -inf by
+// selection before any maximum.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max_xor16_32(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = fmax2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  return fmax2(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 // One 16-byte piece of a pool tile, loaded with the nontemporal hint (the `nt` cache
 // policy): a launch reads each tile exactly once, so the caches need not keep it.  On
@@ -299,10 +304,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
           for (int i = 0; i < 4; ++i)
             if (hide(t, i)) sacc[t][i] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
-                           fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
+      float mx = fmax2(fmax2(fmax2(sacc[0][0], sacc[0][1]), fmax2(sacc[0][2], sacc[0][3])),
+                       fmax2(fmax2(sacc[1][0], sacc[1][1]), fmax2(sacc[1][2], sacc[1][3])));
+      mx = fmax2(mx, fmax2(fmax2(fmax2(sacc[2][0], sacc[2][1]), fmax2(sacc[2][2], sacc[2][3])),
+                           fmax2(fmax2(sacc[3][0], sacc[3][1]), fmax2(sacc[3][2], sacc[3][3]))));
       mx = max_xor16_32(mx);
       // a row with every score hidden keeps its state (its max stays -inf, p = 0)
       const float m_new = fmaxf(m_run, mx * a.scale_log2);
