@@ -89,7 +89,7 @@ def test_verify_rejects_bad_levels_and_workspace():
     s = fake_state()
     assert L.tv_verify_attn(8, 15, P, P, P, P, P, None, ctypes.byref(s), None, P, None, P, 1 << 30, 1, None) == tv.TV_EINVAL  # Hq % Hkv
     need = L.tv_verify_attn_workspace_bytes(8, 16, ctypes.byref(s), 3)
-    # 4 units (2 seq x 2 heads x 1 row block) of 2 + 2 chunks = 16 chunks in 3 slices of 6:
+    # 4 units (2 seq x 2 heads x 1 row block) of 2 + 2 chunks = 16 chunks in 3 slices (5, 5, 6):
     # (slice, unit) pairs are numbered slice + unit < 3 + 4 - 1 -> 6 partial blocks of 64
     # rows x (128 floats + a (max, sum) pair)
     assert need == 6 * 64 * 128 * 4 + 6 * 64 * 8

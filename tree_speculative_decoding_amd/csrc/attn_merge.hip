@@ -7,7 +7,8 @@
 // unit_rows = 64 or 128 query rows), one wave per query row r = node * G + head-in-group, each lane d/64 channels of the row.  The
 // partials of a row are merged across lanes, not one after another: the lanes read the
 // slices' (max, sum) pairs together and reduce the common maximum M, then the partial
-// rows are read 16 at a time with no load waiting on another and summed with weights
+// rows are read 16 at a time (nontemporal after long slices) with no load waiting on
+// another and summed with weights
 // 2^(m_s - M) (slices with an empty sum weigh nothing, by selection).  For the paths
 // whose prefix kernel does not attend the tail and the chain, the D tree tokens of the
 // KV head are staged in LDS, and the chain is the node's ancestor mask: only its set
@@ -19,10 +20,13 @@
 
 namespace tv {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kFinishWaves = 4;   // rows per workgroup
 constexpr int kMergeBatch = 16;   // partial rows read together
 
-template <typename T, int DH>
+// NT: the partials are read with the nontemporal hint (they were written with it).
+template <typename T, int DH, bool NT>
 __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
   constexpr int EPL = DH / 64;  // channels per lane
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
@@ -65,9 +69,9 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
       return;
     }
     // partials of the shared prefix: one per workgroup whose slice touched this unit
-    const long long u = (long long)bg * a.row_blocks + rb;
-    const int n_parts = a.parts > 0 ? unit_part_count(u, a.tmax, a.per) : 0;
-    const long long p0 = a.parts > 0 ? unit_first_part(u, a.tmax, a.per) : 0;
+    const int u = (int)bg * a.row_blocks + rb;
+    const int n_parts = a.parts > 0 ? unit_part_count(a, u) : 0;
+    const int p0 = a.parts > 0 ? unit_first_part(a, u) : 0;
     // with the tail and chain attended by the prefix kernel, a unit it covered with one
     // workgroup is already written; otherwise its partials already hold tail and chain
     if (a.fused_tree && n_parts == 1) return;
@@ -81,7 +85,9 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
     // drop it by selection
     auto slice_ml = [&](int s0) {
       const int s = min(s0 + lane, n_parts - 1);
-      float2 ml = a.ws_ml[row0 + (size_t)s * sstride];
+      const f32x2* src = (const f32x2*)(a.ws_ml + row0 + (size_t)s * sstride);
+      const f32x2 mlv = NT ? __builtin_nontemporal_load(src) : *src;
+      float2 ml = make_float2(mlv.x, mlv.y);
       asm volatile("" ::"v"(ml.x), "v"(ml.y));
       if (s0 + lane >= n_parts) ml.y = 0.f;
       return ml;
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
             ct[t] = t0 + t < cnt ? __shfl(c, tt, 64) : 0.f;
             const float* src = a.ws_o + (row0 + (size_t)(s0 + tt) * sstride) * DH + lane * EPL;
 #pragma unroll
-            for (int x = 0; x < EPL; ++x) v[t][x] = src[x];
+            for (int x = 0; x < EPL; ++x) v[t][x] = NT ? __builtin_nontemporal_load(src + x) : src[x];
           }
           // every load above is issued before any is used (none may move under the
           // selections below)
@@ -210,17 +216,22 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
   }
 }
 
-template <typename T, int DH>
-static hipError_t launch_finish_t(const AttnArgs& a, hipStream_t s) {
+template <typename T, int DH, bool NT>
+static hipError_t launch_finish_nt(const AttnArgs& a, hipStream_t s) {
   const size_t lds = a.fused_tree ? 0 : (size_t)a.D * DH * sizeof(T) * 2;
   if (lds > 65536) {  // beyond the default dynamic-LDS limit (fp32, d = 128, D > 32)
-    hipError_t e = hipFuncSetAttribute((const void*)k_attn_finish<T, DH>,
+    hipError_t e = hipFuncSetAttribute((const void*)k_attn_finish<T, DH, NT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid(a.Hkv * a.row_blocks * (a.unit_rows / kFinishWaves), a.B), block(kFinishWaves * 64);
-  hipLaunchKernelGGL((k_attn_finish<T, DH>), grid, block, lds, s, a);
+  hipLaunchKernelGGL((k_attn_finish<T, DH, NT>), grid, block, lds, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int DH>
+static hipError_t launch_finish_t(const AttnArgs& a, hipStream_t s) {
+  return a.nt_partials ? launch_finish_nt<T, DH, true>(a, s) : launch_finish_nt<T, DH, false>(a, s);
 }
 
 hipError_t launch_attn_finish(const AttnArgs& a, hipStream_t s) {

@@ -8,7 +8,8 @@
 // workgroups (two per CU), or, when a KV head has more than 64 rows (G * D > 64),
 // 128-row units in 8-wave workgroups (one per CU) so that every row of the head shares
 // one stream.  The units' prefixes, cut into 64-entry chunks and laid end to end, are
-// split into equal slices, one persistent workgroup each (one round on the GPU); 16
+// split into slices of equal length to within one chunk, one persistent workgroup each
+// (one round on the GPU); 16
 // query rows per wave (rows r = node * G + head-in-group).  Per 64-entry chunk:
 //   1. the K chunk (64 x 128, row-major) and the V^T tile (128 x 64; the V pool is
 //      stored transposed per 64-entry tile) are each one contiguous 16 KB block,
@@ -43,6 +44,7 @@ namespace tv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 constexpr int kDH = 128;        // head dim handled by this kernel
@@ -133,17 +135,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
   uint4 kpa[PER], vpa[PER], kpb[PER], vpb[PER];
 
   // this workgroup's slice of the units' chunks, laid end to end
-  const long long total = a.units * a.tmax;
-  long long cg = (long long)part * a.per;
-  const long long cend = min(cg + a.per, total);
+  int cg = slice_begin(a, part);
+  const int cend = slice_begin(a, part + 1);
   while (cg < cend) {
-    const long long u = cg / a.tmax;
-    const int c_first = (int)(cg - u * a.tmax);
-    const int c_last = (int)min((long long)a.tmax, cend - u * a.tmax);
+    const int u = cg / a.tmax;
+    const int c_first = cg - u * a.tmax;
+    const int c_last = min(a.tmax, cend - u * a.tmax);
     const bool whole_unit = c_first == 0 && c_last == a.tmax;  // no other workgroup touches it
-    const int rb = (int)(u % a.row_blocks);
-    const int g = (int)((u / a.row_blocks) % a.Hkv);
-    const int b = (int)(u / ((long long)a.row_blocks * a.Hkv));
+    const int rb = u % a.row_blocks;
+    const int g = (u / a.row_blocks) % a.Hkv;
+    const int b = u / (a.row_blocks * a.Hkv);
     const size_t bg = (size_t)b * a.Hkv + g;
 
     // Q^T operand: lane (n16, grp), k-step ks holds Q[row][32ks + 8grp .. +7]
@@ -571,9 +572,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_mfma(AttnArgs
       } else {
         const size_t wrow = partial_row(a, part, u, w * 16 + n16);
         float* o = a.ws_o + wrow * kDH;
+        if (a.nt_partials) {  // long slices: stream the partials past the caches (uniform)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *(f32x4*)(o + 16 * dt + 4 * grp) = oacc[dt];
-        if (grp == 0) a.ws_ml[wrow] = make_float2(m_run, l_run);
+          for (int dt = 0; dt < 8; ++dt) __builtin_nontemporal_store(oacc[dt], (f32x4*)(o + 16 * dt + 4 * grp));
+          if (grp == 0) __builtin_nontemporal_store(f32x2{m_run, l_run}, (f32x2*)(a.ws_ml + wrow));
+        } else {
+          // (keeps the compiler from merging the two branches' stores into one without the hint)
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) *(f32x4*)(o + 16 * dt + 4 * grp) = oacc[dt];
+          if (grp == 0) a.ws_ml[wrow] = make_float2(m_run, l_run);
+          asm volatile("" ::: "memory");
+        }
       }
     }
     cg = u * a.tmax + c_last;

@@ -28,16 +28,15 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   const int r_loc = tid >> 2, part = tid & 3;
   const T* q = (const T*)a.q;
 
-  const long long total = a.units * a.tmax;
-  long long cg = (long long)blockIdx.x * a.per;
-  const long long cend = min(cg + a.per, total);
+  int cg = slice_begin(a, blockIdx.x);
+  const int cend = slice_begin(a, blockIdx.x + 1);
   while (cg < cend) {
-    const long long u = cg / a.tmax;
-    const int c_first = (int)(cg - u * a.tmax);
-    const int c_last = (int)min((long long)a.tmax, cend - u * a.tmax);
-    const int rb = (int)(u % a.row_blocks);
-    const int g = (int)((u / a.row_blocks) % a.Hkv);
-    const int b = (int)(u / ((long long)a.row_blocks * a.Hkv));
+    const int u = cg / a.tmax;
+    const int c_first = cg - u * a.tmax;
+    const int c_last = min(a.tmax, cend - u * a.tmax);
+    const int rb = u % a.row_blocks;
+    const int g = (u / a.row_blocks) % a.Hkv;
+    const int b = u / (a.row_blocks * a.Hkv);
     const size_t bg = (size_t)b * a.Hkv + g;
     const int row = rb * RBLK + r_loc;
 

@@ -134,16 +134,19 @@ struct AttnArgs {
   // Prefix-stream partition.  A unit is one (sequence, KV head, block of unit_rows query
   // rows); its prefix is `tmax` 64-entry chunks long (a bound from the pool capacities;
   // chunks past a sequence's committed entries are empty).  The units' chunks, laid end
-  // to end, are cut into `parts` equal slices of `per` chunks, one workgroup each.  A
+  // to end, are cut into `parts` slices of equal length to within one chunk (slice_begin),
+  // one workgroup each.  A
   // slice touches a run of consecutive units, and consecutive slices share at most one
   // unit, so (slice p, unit u) pairs are numbered uniquely by p + u (< parts + units - 1):
   // the partial of that pair is the workspace's row block p + u (partial_row()).
   int unit_rows;                     // query rows of a unit: 64, or 128 for the 8-wave MFMA instance
   int row_blocks;                    // RB = ceil(R / unit_rows)
   int tmax;                          // chunks per unit
-  long long units;                   // B * Hkv * RB
+  int units;                         // B * Hkv * RB (units * tmax < 2^31)
   int parts;                         // workgroups of the prefix stream
-  long long per;                     // chunks per workgroup
+  int total;                         // units * tmax chunk slots
+  int idx32;                         // parts * total < 2^32: slice arithmetic in 32 bits
+  int nt_partials;                   // partials written and read with the nontemporal hint
   int fused_tree;                    // the MFMA prefix kernel also attends to the raw tail and
                                      // the tree chunk, and writes whole units' rows itself
   int tree_tiles;                    // 16-entry tiles of that chunk: 1, 2 or 4
@@ -180,12 +183,23 @@ __device__ __forceinline__ void chunk_entries(int n0, int T0, int n1, int c, int
   }
 }
 
-// first workgroup whose slice touches unit u, and how many workgroups touch it
-__device__ __forceinline__ long long unit_first_part(long long u, int tmax, long long per) {
-  return u * tmax / per;
+// Slice p of the prefix stream is the chunks [p * total / parts, (p + 1) * total / parts)
+// of the units' chunks laid end to end (1 <= parts <= total < 2^31): slice lengths differ by
+// at most one chunk, so every workgroup of the one round has the same work to within a
+// chunk.  In 32-bit arithmetic when parts * total < 2^32 (idx32, set on the host).
+__device__ __forceinline__ int slice_begin(const AttnArgs& a, int p) {
+  if (a.idx32) return (int)((uint32_t)p * (uint32_t)a.total / (uint32_t)a.parts);
+  return (int)((long long)p * a.total / a.parts);
 }
-__device__ __forceinline__ int unit_part_count(long long u, int tmax, long long per) {
-  return (int)((u * tmax + tmax - 1) / per - u * tmax / per + 1);
+// the slice holding chunk x (the largest p with slice_begin(p) <= x)
+__device__ __forceinline__ int slice_of(const AttnArgs& a, int x) {
+  if (a.idx32) return (int)(((uint32_t)x * (uint32_t)a.parts + (uint32_t)a.parts - 1u) / (uint32_t)a.total);
+  return (int)(((long long)x * a.parts + a.parts - 1) / a.total);
+}
+// first workgroup whose slice touches unit u, and how many workgroups touch it
+__device__ __forceinline__ int unit_first_part(const AttnArgs& a, int u) { return slice_of(a, u * a.tmax); }
+__device__ __forceinline__ int unit_part_count(const AttnArgs& a, int u) {
+  return slice_of(a, u * a.tmax + a.tmax - 1) - slice_of(a, u * a.tmax) + 1;
 }
 
 }  // namespace tv

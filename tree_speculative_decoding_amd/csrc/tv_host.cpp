@@ -121,7 +121,10 @@ struct Plan {
   bool fused_tree;  // the MFMA kernel attends to the raw tail and the tree chunk itself
   int tree_tiles;   // 16-entry tiles of that chunk
   int R, unit_rows, row_blocks, tmax, parts;
-  long long units, per;
+  long long per_lo;  // chunks per slice, rounded down
+  long long units;
+  bool too_big;     // units * tmax chunk slots do not fit the kernels' 32-bit indices
+  bool nt_partials; // partials are written and read with the nontemporal hint
   bool all_whole;   // every unit is one workgroup's and the prefix kernel writes the rows: no partials
   size_t ws_o_bytes, ws_ml_off, total;
   bool fold;        // the MFMA prefix launch has room for the scratch pad's B*D workgroups ahead of the stream
@@ -149,9 +152,9 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   for (int l = 0; l < st->n_levels; ++l) p.tmax += (st->lvl[l].cap + 63) / 64;
   p.units = (long long)st->B * st->Hkv * p.row_blocks;
   const long long total = p.units * p.tmax;
-  if (total == 0) {
+  p.too_big = total > 0x7fffffffLL;
+  if (total == 0 || p.too_big) {
     p.parts = 0;
-    p.per = 1;
   } else {
     long long want;
     const bool wide = p.unit_rows == 128;
@@ -178,16 +181,31 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
     p.pad_after = !wide && !p.fold;
     if (want > total) want = total;
     if (want < 1) want = 1;
-    p.per = (total + want - 1) / want;
-    p.parts = (int)((total + p.per - 1) / p.per);
+    // With at least one slice per unit, a multiple of the unit count puts every slice
+    // boundary on a unit boundary or inside one unit, so no slice straddles two units
+    // (each unit then has the same number of slices, and no workgroup starts a second
+    // unit's prefix or writes two partials); taken when it keeps >= 7/8 of the slots.
+    if (num_parts == 0 && want >= p.units) {
+      const long long aligned = want / p.units * p.units;
+      if (aligned * 8 >= want * 7) want = aligned;
+    }
+    p.parts = (int)want;  // slices of total / parts chunks, to within one (slice_begin)
+    p.per_lo = total / want;
   }
+  // Partials after long slices (8 chunks or more, i.e. long prefixes at small batch) are
+  // written and read back with the nontemporal hint: measured 1-2 us faster per call at a
+  // 131072-token prefix and batch 1, and 0.5-1 us slower after 4-chunk slices (batch 4-8 at
+  // 4096-8192 tokens), whose partials the merge still finds in the caches.
+  p.nt_partials = p.mfma && p.parts > 0 && p.per_lo >= 8;
   // the tail (< C0 tokens) and the D tree tokens form one extra chunk of at most 64
   // entries, attended in 16-entry tiles
   const int c0 = st->n_levels > 0 ? st->lvl[0].C : 1;
   const int tree_entries = D + (c0 - 1);
   p.fused_tree = p.mfma && p.parts > 0 && tree_entries <= 64;
   p.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
-  p.all_whole = p.fused_tree && p.per % p.tmax == 0;
+  // every slice a whole number of units: each slice boundary a multiple of tmax
+  p.all_whole = p.fused_tree && p.parts > 0;
+  for (long long q = 1; p.all_whole && q < p.parts; ++q) p.all_whole = q * total / p.parts % p.tmax == 0;
   // partials: one row block per (slice, unit) pair, numbered slice + unit
   const size_t rows = p.all_whole || p.parts == 0 ? 0 : (size_t)(p.parts + p.units - 1) * p.unit_rows;
   p.ws_o_bytes = round256(rows * st->d * sizeof(float));
@@ -223,6 +241,7 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
         return fail(TV_EINVAL, "scratch level %d must be 16-byte aligned", l);
     }
   const Plan p = make_plan(D, Hq, st, num_parts);
+  if (p.too_big) return fail(TV_EUNSUPPORTED, "B * Hkv * row blocks * capacity chunks exceeds 2^31 - 1");
   if (workspace == nullptr || workspace_bytes < p.total)
     return fail(TV_EWORKSPACE, "workspace %zu bytes, need %zu", workspace == nullptr ? (size_t)0 : workspace_bytes,
                 p.total);
@@ -243,7 +262,10 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
   a.out = out; a.lse = lse;
   if (scratch != nullptr) a.scratch = *scratch;
   a.build_scratch = scratch != nullptr;
-  a.unit_rows = p.unit_rows; a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = p.units; a.parts = p.parts; a.per = p.per;
+  a.unit_rows = p.unit_rows; a.row_blocks = p.row_blocks; a.tmax = p.tmax; a.units = (int)p.units; a.parts = p.parts;
+  a.total = (int)(p.units * p.tmax);
+  a.idx32 = (unsigned long long)p.parts * (unsigned long long)a.total < (1ull << 32);
+  a.nt_partials = p.nt_partials;
   a.ws_o = (float*)workspace;
   a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
   a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);
@@ -323,7 +345,8 @@ TV_API size_t tv_verify_attn_workspace_bytes(int D, int Hq, const tv_state* st, 
   if (D < 1 || D > TV_MAX_D || Hq < 1 || num_parts < 0) return 0;
   if (check_state(st) != TV_OK) return 0;
   if (Hq % st->Hkv != 0) return 0;
-  return make_plan(D, Hq, st, num_parts).total;
+  const Plan p = make_plan(D, Hq, st, num_parts);
+  return p.too_big ? 0 : p.total;
 }
 
 TV_API tv_status tv_verify_attn(int D, int Hq, const void* q, const void* k_tree, const void* v_tree,
@@ -346,7 +369,9 @@ TV_API tv_status tv_verify_attn_noalloc(int D, int Hq, const void* q, const void
   if (D < 1 || D > TV_MAX_D) return fail(TV_EINVAL, "D = %d outside 1..%d", D, TV_MAX_D);
   if (Hq < 1 || Hq % st->Hkv != 0) return fail(TV_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, st->Hkv);
   if (num_parts < 0) return fail(TV_EINVAL, "num_parts = %d < 0", num_parts);
-  const size_t need = make_plan(D, Hq, st, num_parts).total;
+  const Plan plan = make_plan(D, Hq, st, num_parts);
+  if (plan.too_big) return fail(TV_EUNSUPPORTED, "B * Hkv * row blocks * capacity chunks exceeds 2^31 - 1");
+  const size_t need = plan.total;
   if (need > TV_NOALLOC_SCRATCH_BYTES)
     return fail(TV_EWORKSPACE, "this shape needs %zu bytes of split-prefix partials; tv_verify_attn_noalloc has %zu "
                 "(use tv_verify_attn with a workspace, or more sequences per call so fewer prefixes are split)",
