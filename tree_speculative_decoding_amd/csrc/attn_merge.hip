@@ -21,6 +21,7 @@
 namespace tv {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFinishWaves = 4;   // rows per workgroup
 constexpr int kMergeBatch = 16;   // partial rows read together
@@ -216,6 +217,159 @@ __global__ __launch_bounds__(kFinishWaves * 64) void k_attn_finish(AttnArgs a) {
   }
 }
 
+// The merge of split units on the MFMA path, whose prefix kernel already attended the raw
+// tail and the chain and wrote the rows of whole units itself: a unit's row of n slices is
+// spread over SG groups of 32 threads (slices sg, sg + SG, ...; each thread 4 channels), so
+// every (max, sum) pair and partial row the thread needs (at most JR) is loaded in one round
+// before any is used; the groups of a row combine their maxima, then their weighted sums,
+// through LDS in group order.  8 / SG rows per 256-thread workgroup.  The summation order
+// depends only on n and SG, so results do not depend on timing.  Rows of more than SG * JR
+// slices (only with very many workgroups per unit) read the rest in further rounds.
+template <int SG, int JR, bool NT>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  constexpr int DH = 128;
+  constexpr int RPW = 8 / SG;  // rows per workgroup
+  __shared__ float red_m[8], red_l[8];
+  __shared__ __attribute__((aligned(16))) f32x4 red_o[8][DH / 4];
+
+  const int tid = threadIdx.x, lane = tid & 31, grp = tid >> 5;
+  const int slot = grp / SG, sg = grp - slot * SG;
+  const int groups = a.unit_rows / RPW;  // workgroups per unit
+  const int g = blockIdx.x % a.Hkv;
+  const int rb = blockIdx.x / a.Hkv / groups;
+  const int rg = blockIdx.x / a.Hkv % groups;
+  const int b = blockIdx.y;
+  const int u = (b * a.Hkv + g) * a.row_blocks + rb;
+  const int n = unit_part_count(a, u);
+  if (n == 1) return;  // a whole unit (uniform): the prefix kernel wrote its rows
+  const int lrow = rg * RPW + slot;       // row within the unit
+  const int r = rb * a.unit_rows + lrow;  // row r = node * G + head-in-group of KV head g
+  const bool valid = r < a.R;             // (the workspace holds every row of a unit: in bounds)
+  const int32_t st = a.seq_err != nullptr ? a.seq_err[b] : TV_SEQ_OK;
+  const size_t row0 = partial_row(a, unit_first_part(a, u), u, lrow);  // slice s: row0 + s * unit_rows
+  const int JT = (n + SG - 1) / SG;  // slices per group, rounded up
+
+  auto ld_o = [&](int s) -> f32x4 {
+    const f32x4* p = (const f32x4*)(a.ws_o + (row0 + (size_t)s * a.unit_rows) * DH) + lane;
+    return NT ? __builtin_nontemporal_load(p) : *p;
+  };
+  auto ld_ml = [&](int s) -> f32x2 {
+    const f32x2* p = (const f32x2*)(a.ws_ml + row0 + (size_t)s * a.unit_rows);
+    return NT ? __builtin_nontemporal_load(p) : *p;
+  };
+  // first round: slices sg + j * SG (j < JR), past n clamped to the last and weighed 0
+  f32x4 ov[JR];
+  f32x2 mlv[JR];
+#pragma unroll
+  for (int j = 0; j < JR; ++j) {
+    const int s = min(sg + j * SG, n - 1);
+    ov[j] = ld_o(s);
+    mlv[j] = ld_ml(s);
+  }
+  // every load above is issued before any is used
+#pragma unroll
+  for (int j = 0; j < JR; ++j) asm volatile("" ::"v"(ov[j]), "v"(mlv[j]));
+  float mt = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < JR; ++j)
+    if (sg + j * SG < n && mlv[j].y > 0.f) mt = fmaxf(mt, mlv[j].x);
+  for (int j = JR; j < JT; ++j) {  // further rounds (rare): their maxima
+    const int s = sg + j * SG;
+    if (s < n) {
+      const f32x2 ml = ld_ml(s);
+      if (ml.y > 0.f) mt = fmaxf(mt, ml.x);
+    }
+  }
+  float M = mt;
+  if (SG > 1) {
+    if (lane == 0) red_m[grp] = mt;
+    __syncthreads();
+    M = red_m[slot * SG];
+#pragma unroll
+    for (int i = 1; i < SG; ++i) M = fmaxf(M, red_m[slot * SG + i]);
+  }
+  // weighted sums in slice order: weights 2^(m_s - M), empty slices weigh nothing
+  f32x4 ot = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lt = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < JR; ++j) {
+      const float c = sg + j * SG < n && mlv[j].y > 0.f ? exp2f(mlv[j].x - M) : 0.f;
+      if (c > 0.f) {
+        lt = fmaf(c, mlv[j].y, lt);
+        ot[0] = fmaf(c, ov[j][0], ot[0]);
+        ot[1] = fmaf(c, ov[j][1], ot[1]);
+        ot[2] = fmaf(c, ov[j][2], ot[2]);
+        ot[3] = fmaf(c, ov[j][3], ot[3]);
+      }
+    }
+    for (int j = JR; j < JT; ++j) {
+      const int s = sg + j * SG;
+      if (s < n) {
+        const f32x2 ml = ld_ml(s);
+        if (ml.y > 0.f) {
+          const float c = exp2f(ml.x - M);
+          const f32x4 o = ld_o(s);
+          lt = fmaf(c, ml.y, lt);
+          ot[0] = fmaf(c, o[0], ot[0]);
+          ot[1] = fmaf(c, o[1], ot[1]);
+          ot[2] = fmaf(c, o[2], ot[2]);
+          ot[3] = fmaf(c, o[3], ot[3]);
+        }
+      }
+    }
+  }
+  if (SG > 1) {
+    red_o[grp][lane] = ot;
+    if (lane == 0) red_l[grp] = lt;
+    __syncthreads();
+    if (sg != 0) return;
+    ot = red_o[slot * SG][lane];
+    lt = red_l[slot * SG];
+#pragma unroll
+    for (int i = 1; i < SG; ++i) {
+      const f32x4 o = red_o[slot * SG + i][lane];
+      ot[0] += o[0]; ot[1] += o[1]; ot[2] += o[2]; ot[3] += o[3];
+      lt += red_l[slot * SG + i];
+    }
+  }
+  if (!valid) return;
+  const int node = r / a.G, head = g * a.G + (r - node * a.G);
+  uint16_t* out = (uint16_t*)a.out + (((size_t)b * a.D + node) * a.Hq + head) * DH + 4 * lane;
+  const size_t li = ((size_t)b * a.D + node) * a.Hq + head;
+  if (st != TV_SEQ_OK) {
+    *(uint2*)out = make_uint2(0u, 0u);
+    if (a.lse != nullptr && lane == 0) a.lse[li] = -INFINITY;
+    return;
+  }
+  const float inv = 1.0f / lt;
+  uint2 pk;
+  pk.x = (uint32_t)f32_to_bf16_bits(ot[0] * inv) | ((uint32_t)f32_to_bf16_bits(ot[1] * inv) << 16);
+  pk.y = (uint32_t)f32_to_bf16_bits(ot[2] * inv) | ((uint32_t)f32_to_bf16_bits(ot[3] * inv) << 16);
+  *(uint2*)out = pk;
+  if (a.lse != nullptr && lane == 0) a.lse[li] = (M + log2f(lt)) * kLn2;
+}
+
+template <int SG, int JR>
+static hipError_t launch_merge_t(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.Hkv * a.row_blocks * (a.unit_rows / (8 / SG)), a.B);
+  if (a.nt_partials) hipLaunchKernelGGL((k_attn_merge<SG, JR, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_attn_merge<SG, JR, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// slices per unit at most n_max: the fewest groups per row that keep a thread at <= 4 loads
+// (up to 32 slices), then more loads per thread
+static hipError_t launch_merge(const AttnArgs& a, hipStream_t s) {
+  const int n = a.merge_nmax;
+  if (n <= 4) return launch_merge_t<1, 4>(a, s);
+  if (n <= 8) return launch_merge_t<2, 4>(a, s);
+  if (n <= 16) return launch_merge_t<4, 4>(a, s);
+  if (n <= 32) return launch_merge_t<8, 4>(a, s);
+  if (n <= 64) return launch_merge_t<8, 8>(a, s);
+  return launch_merge_t<8, 16>(a, s);
+}
+
 template <typename T, int DH, bool NT>
 static hipError_t launch_finish_nt(const AttnArgs& a, hipStream_t s) {
   const size_t lds = a.fused_tree ? 0 : (size_t)a.D * DH * sizeof(T) * 2;
@@ -236,6 +390,7 @@ static hipError_t launch_finish_t(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attn_finish(const AttnArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
+  if (a.fused_tree) return launch_merge(a, s);  // (the MFMA path: bf16, d = 128)
   if (a.dtype == TV_BF16) return a.d == 128 ? launch_finish_t<uint16_t, 128>(a, s) : launch_finish_t<uint16_t, 64>(a, s);
   return a.d == 128 ? launch_finish_t<float, 128>(a, s) : launch_finish_t<float, 64>(a, s);
 }

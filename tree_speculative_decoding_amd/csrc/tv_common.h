@@ -147,6 +147,7 @@ struct AttnArgs {
   int total;                         // units * tmax chunk slots
   int idx32;                         // parts * total < 2^32: slice arithmetic in 32 bits
   int nt_partials;                   // partials written and read with the nontemporal hint
+  int merge_nmax;                    // a bound on the slices of one unit (the merge's shape)
   int fused_tree;                    // the MFMA prefix kernel also attends to the raw tail and
                                      // the tree chunk, and writes whole units' rows itself
   int tree_tiles;                    // 16-entry tiles of that chunk: 1, 2 or 4

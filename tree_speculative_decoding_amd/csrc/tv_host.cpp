@@ -3,6 +3,7 @@
 // that can be made on the host happens before the first launch of a call.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <mutex>
@@ -266,6 +267,9 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
   a.total = (int)(p.units * p.tmax);
   a.idx32 = (unsigned long long)p.parts * (unsigned long long)a.total < (1ull << 32);
   a.nt_partials = p.nt_partials;
+  // slices touching one unit: its tmax chunks span at most (tmax - 1) / per_lo + 2 slices (a
+  // bound of the slice length alone, so that batches cut the same way per unit merge alike)
+  a.merge_nmax = p.parts > 0 ? (int)std::min<long long>(1 << 20, (p.tmax - 1) / p.per_lo + 2) : 0;
   a.ws_o = (float*)workspace;
   a.ws_ml = (float2*)((char*)workspace + p.ws_ml_off);
   a.scale_log2 = tv::kLog2e / std::sqrt((float)st->d);
