@@ -172,6 +172,14 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
       want = slots;
       const long long by_size = (total + 3) / 4;
       if (want > by_size) want = by_size;
+      // A stream of 16 to 32 chunks per CU runs one slice per CU rather than two shorter
+      // ones: each split slice writes a partial of one chunk's size that the merge reads back
+      // (6% of a 16-chunk slice, 12% of an 8-chunk one).  Exactly one per CU: a few CUs with
+      // two stream workgroups would finish last.  At batch 1 and a 131072-token prefix
+      // (16.5 chunks per CU): 256 slices 40.3-40.6 us per call against 41.2-41.9 us for 504,
+      // 43.9 us for 264.
+      const long long cus = device_cus();
+      if (!wide && total >= 16 * cus && total < 32 * cus && want > cus) want = cus;
       if (!wide && want + pad <= slots) {
         p.fold = true;
       } else if (!wide && pad <= 16 && pad < want) {
