@@ -147,8 +147,10 @@ def find_workload(name: str):
 
 
 PREFIX_KERNEL = "tv::k_attn_mfma<4, 1, false>"  # the contiguous-pool instance the benchmark runs
-STEP_KERNELS = ("k_tree_mask", "k_scratch", "k_attn_mfma", "k_attn_finish", "k_accept", "k_refresh")
-CALL_KERNELS = ("k_scratch", "k_attn_mfma", "k_attn_finish")  # what one tv_verify_attn call launches
+STEP_KERNELS = ("k_tree_mask", "k_scratch", "k_attn_mfma", "k_attn_merge", "k_attn_finish", "k_accept", "k_refresh")
+# what one tv_verify_attn call launches (k_attn_merge: split prefixes on the MFMA path;
+# k_attn_finish: the vector-ALU path's merge)
+CALL_KERNELS = ("k_scratch", "k_attn_mfma", "k_attn_merge", "k_attn_finish")
 
 
 def _short(name: str) -> str:
