@@ -125,6 +125,23 @@ def test_partition_invariance(name, parts):
     check_scratch(res)
 
 
+# one sequence, one KV head, a 32768-token prefix: a single unit of 134 chunk slots
+LONG_ONE = synth.Workload("long_one", 1, 8, 8, 1, 128, "bf16", (4, 128), 32768, 2, 3, 0.6, 1503)
+
+
+@pytest.mark.parametrize("parts", [5, 10, 20, 40, 100, 1000])
+def test_merge_shapes(parts):
+    """One prefix split over 5 .. 134 slices: the merge of split prefixes spreads a row's
+    slices over 2, 4 or 8 thread groups, reads 4, 8 or 16 slices per thread in one round,
+    and beyond 128 slices (1000 requested: one chunk each) reads the rest in further
+    rounds; slices of 8 chunks or more (5 and 10) store and read their partials with the
+    nontemporal hint.  Every case matches the oracle."""
+    _say(f"verify long_one parts={parts}")
+    res = run_verify(LONG_ONE, num_parts=parts)
+    check_outputs(res)
+    check_scratch(res)
+
+
 @pytest.mark.parametrize("name,parts", [("linear", 100), ("tree", 100), ("linear", 0), ("tree", 0)])
 def test_pool_headroom(name, parts):
     """The same committed history in pools with about 4x headroom: three quarters of the
