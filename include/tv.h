@@ -190,9 +190,11 @@ TV_API tv_status tv_build_draft_tree(int B, int topk, int steps, int D, int voca
 
 /*
  * Bytes of device workspace tv_verify_attn needs for this state shape when the
- * shared-prefix stream is cut into num_parts equal slices, one workgroup each
- * (0 = the library's choice for the current device: one full round of resident
- * workgroups; the same value must then be passed to tv_verify_attn).  The slices run
+ * shared-prefix stream is cut into num_parts slices of equal length to within one
+ * 64-entry chunk, one workgroup each (0 = the library's choice for the current device:
+ * one full round of resident workgroups, at least 4 chunks each, as a multiple of the
+ * prefix count where that keeps 7/8 of them, and one per compute unit for streams of 16
+ * to 32 chunks per unit; the same value must then be passed to tv_verify_attn).  The slices run
  * over every (sequence, KV head, block of query rows) prefix laid end to end, so any
  * batch size keeps the whole GPU busy; a prefix split over several slices gets one
  * partial (max, sum, unnormalised output) per slice, merged after the stream.  When no
