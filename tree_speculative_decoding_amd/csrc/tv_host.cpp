@@ -212,9 +212,12 @@ Plan make_plan(int D, int Hq, const tv_state* st, int num_parts) {
   const int tree_entries = D + (c0 - 1);
   p.fused_tree = p.mfma && p.parts > 0 && tree_entries <= 64;
   p.tree_tiles = tree_entries <= 16 ? 1 : tree_entries <= 32 ? 2 : 4;
-  // every slice a whole number of units: each slice boundary a multiple of tmax
-  p.all_whole = p.fused_tree && p.parts > 0;
-  for (long long q = 1; p.all_whole && q < p.parts; ++q) p.all_whole = q * total / p.parts % p.tmax == 0;
+  // every slice a whole number of units: each slice boundary a multiple of tmax (never with
+  // more slices than units; always when the slice count divides the unit count; else checked
+  // boundary by boundary)
+  p.all_whole = p.fused_tree && p.parts > 0 && p.parts <= p.units;
+  if (p.all_whole && p.units % p.parts != 0)
+    for (long long q = 1; p.all_whole && q < p.parts; ++q) p.all_whole = q * total / p.parts % p.tmax == 0;
   // partials: one row block per (slice, unit) pair, numbered slice + unit
   const size_t rows = p.all_whole || p.parts == 0 ? 0 : (size_t)(p.parts + p.units - 1) * p.unit_rows;
   p.ws_o_bytes = round256(rows * st->d * sizeof(float));
