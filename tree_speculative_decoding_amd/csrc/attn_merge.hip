@@ -1,21 +1,24 @@
 // Branch-aware verify attention, final step (TSD-V4 §3.1: a candidate sees the accepted
 // context and the ancestors on its own branch, never candidates of other branches):
-// merge the prefix-stream partials of a query row, add the finest level's raw tail and
-// the node's own chain, and normalise.
+// merge the prefix-stream partials of a query row (weights 2^(m_s - M) over the row's
+// slices, slices with an empty sum weighing nothing, by selection), and normalise.
 //
-// One workgroup of 4 waves per (sequence, KV head, 4 rows of a unit's block of
-// unit_rows = 64 or 128 query rows), one wave per query row r = node * G + head-in-group, each lane d/64 channels of the row.  The
-// partials of a row are merged across lanes, not one after another: the lanes read the
-// slices' (max, sum) pairs together and reduce the common maximum M, then the partial
-// rows are read 16 at a time (nontemporal after long slices) with no load waiting on
-// another and summed with weights
-// 2^(m_s - M) (slices with an empty sum weigh nothing, by selection).  For the paths
-// whose prefix kernel does not attend the tail and the chain, the D tree tokens of the
-// KV head are staged in LDS, and the chain is the node's ancestor mask: only its set
-// bits are read, so K/V of other branches never enter the arithmetic (excluded by
-// selection, not by a -inf score).  Chain scores are reduced eight at a time with
-// interleaved shuffles, then folded into the same base-2 online softmax as the prefix
-// kernels.
+// k_attn_merge: the MFMA path, whose prefix kernel already attended the raw tail and the
+// chain; a row's slices spread over groups of 32 threads, every load of a thread in one
+// round, the groups combined through LDS (see the kernel).
+//
+// k_attn_finish: every other path (the fp32 vector kernel, d = 64, trees whose tail +
+// tree chunk exceeds 64 entries).  One workgroup of 4 waves per (sequence, KV head, 4
+// rows of a unit's block of unit_rows = 64 or 128 query rows), one wave per query row
+// r = node * G + head-in-group, each lane d/64 channels of the row.  The partials of a
+// row are merged across lanes, not one after another: the lanes read the slices' (max,
+// sum) pairs together and reduce the common maximum M, then the partial rows are read 16
+// at a time (nontemporal after long slices) with no load waiting on another.  Then the
+// finest level's raw tail and the node's own chain: the D tree tokens of the KV head are
+// staged in LDS, and the chain is the node's ancestor mask: only its set bits are read,
+// so K/V of other branches never enter the arithmetic (excluded by selection, not by a
+// -inf score).  Chain scores are reduced eight at a time with interleaved shuffles, then
+// folded into the same base-2 online softmax as the prefix kernels.
 #include "tv_launch.h"
 
 namespace tv {

@@ -168,7 +168,7 @@ __device__ __forceinline__ size_t partial_row(const AttnArgs& a, long long part,
 }
 
 // The prefix of a (sequence, KV head) is streamed as 64-entry chunks: level 0's
-// ceil(n0/64) chunks, then level 1's.  Splits take equal runs of chunks, so a
+// ceil(n0/64) chunks, then level 1's.  Slices take runs of whole chunks, so a
 // chunk never straddles two levels and always starts 64-aligned in its pool.
 // chunk c of a sequence's concatenated pools -> (level, first entry, entry count)
 __device__ __forceinline__ void chunk_entries(int n0, int T0, int n1, int c, int* lvl,
