@@ -58,7 +58,7 @@ extern "C" {
 #define TV_API
 #endif
 
-#define TV_VERSION 130      /* 1.3.0: workspace holds only the partials of split prefixes */
+#define TV_VERSION 140      /* 1.4.0: tv_scratch.deferred (levels brought up to date by the refresh) */
 #define TV_MAX_LEVELS 2
 #define TV_MAX_D 64
 #define TV_TILE_RUN 16     /* tiles of one (sequence, KV head) kept together in a contiguous pool */
@@ -142,13 +142,25 @@ typedef struct {
  * below the capacity whose page exists are written.  tv_refresh_state / tv_accept_refresh
  * given the same struct then copy only the committed entries of nodes outside the mask.
  * The resulting state is bit-identical to the one without in_place, apart from pool
- * slots at or beyond the new counts (never read). */
+ * slots at or beyond the new counts (never read).
+ *
+ * deferred (TSD-V4 §4.3: C4 and C128 have different refresh schedules; the coarse level is
+ * compressed rarely, so its cache writes can be delayed and combined once the accepted
+ * path is known): bit l set = level l gets no scratch states.  tv_verify_attn builds none
+ * for it (its four pointers may be NULL) and writes none of its entries in place;
+ * tv_refresh_state / tv_accept_refresh then bring that level up to date from the accepted
+ * path's own tokens in one pass: the committed open sum plus the path tokens in path
+ * order in fp32, each block the path closes written once as sum / C (one rounding), the
+ * rest left as the new open sum.  The additions and roundings are those the scratch pad
+ * makes along the same chain, so the state is bit-identical to the one without deferral.
+ * Bits at or beyond n_levels are invalid (TV_EINVAL). */
 typedef struct {
   void* entry_k[TV_MAX_LEVELS];   /* [B][D][Hkv][d] element dtype */
   void* entry_v[TV_MAX_LEVELS];   /* [B][D][Hkv][d] */
   float* open_k[TV_MAX_LEVELS];   /* [B][D][Hkv][d] fp32 */
   float* open_v[TV_MAX_LEVELS];   /* [B][D][Hkv][d] */
   uint64_t* in_place;             /* [B] out of tv_verify_attn, in to the refresh; NULL = off */
+  uint32_t deferred;              /* levels updated from the accepted path by the refresh (bit l) */
 } tv_scratch;
 
 /*

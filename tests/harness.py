@@ -125,7 +125,7 @@ def upload_step(s: synth.StepInputs, dtype: str) -> DevStep:
 class Runner:
     """Owns the per-step device buffers of one (B, D, Hq) shape and runs the four calls."""
 
-    def __init__(self, st, D: int, Hq: int, num_parts: int = 0, in_place: bool = True):
+    def __init__(self, st, D: int, Hq: int, num_parts: int = 0, in_place: bool = True, deferred: int = 0):
         import torch
         import tree_speculative_decoding_amd as tv
         self.st, self.D, self.Hq = st, D, Hq
@@ -140,7 +140,7 @@ class Runner:
         self.path = torch.zeros(B, D, dtype=torch.int32, device=dev)
         self.bonus = torch.zeros(B, dtype=torch.int32, device=dev)
         self.log = torch.zeros(B, max(len(st.levels), 1), D, 2, dtype=torch.int32, device=dev)
-        self.sc = tv.DeviceScratch(B, D, Hkv, d, st.dtype, len(st.levels), in_place=in_place)
+        self.sc = tv.DeviceScratch(B, D, Hkv, d, st.dtype, len(st.levels), in_place=in_place, deferred=deferred)
         self.num_parts = num_parts
         nbytes = tv.tv_verify_attn_workspace_bytes(D, Hq, st, num_parts)
         assert nbytes > 0

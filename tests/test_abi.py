@@ -15,7 +15,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 10
     for n in names:
         assert hasattr(L, n), n
-    assert tv.tv_version() == 130
+    assert tv.tv_version() == 140
 
 
 def test_struct_layout_matches_header():
@@ -24,7 +24,7 @@ def test_struct_layout_matches_header():
     assert tv.tv.TvLevel.page_table.offset == 48 and tv.tv.TvLevel.num_pages.offset == 60
     assert ctypes.sizeof(TvState) == 176
     assert TvState.lvl.offset == 24 and TvState.P.offset == 168
-    assert ctypes.sizeof(TvScratch) == 72 and TvScratch.in_place.offset == 64
+    assert ctypes.sizeof(TvScratch) == 80 and TvScratch.in_place.offset == 64 and TvScratch.deferred.offset == 72
 
 
 def fake_state(**kw):
@@ -109,6 +109,10 @@ def test_refresh_and_compress_reject_bad_args():
     assert L.tv_refresh_state(8, ctypes.byref(s), None, P, P, P, P, None, P, None) == tv.TV_EINVAL  # no scratch
     sc = TvScratch()
     assert L.tv_refresh_state(8, ctypes.byref(s), ctypes.byref(sc), P, P, P, P, None, P, None) == tv.TV_EINVAL
+    # every level deferred: no scratch pointers are needed, but a bit past n_levels is refused
+    sc.deferred = 0x4
+    assert L.tv_refresh_state(8, ctypes.byref(s), ctypes.byref(sc), P, P, P, P, None, P, None) == tv.TV_EINVAL
+    assert b"n_levels" in L.tv_last_error()
     assert L.tv_compress_prefix(ctypes.byref(s), P, P, -1, P, None) == tv.TV_EINVAL
     assert L.tv_compress_prefix(ctypes.byref(s), None, P, 10, P, None) == tv.TV_EINVAL
 

@@ -217,24 +217,17 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("name,fused,paged", [(n, False, False) for n in IN_PLACE] +
-                         [("bf16_tree_c4_c128", True, False), ("bf16_chain_c4_c128", False, True)])
-def test_in_place_chain_equals_copy_path(name, fused, paged):
-    """The refresh skip (TSD-V4 §4.3): with scratch.in_place the verify writes the deepest
-    chain's closing entries straight into their pool slots and the refresh copies only the
-    other accepted nodes' entries.  Step after step the run matches the run without it bit
-    for bit -- acceptance, commit log, status, counts, open sums, tails and every committed
-    pool entry -- and the oracle; in_place[b] is the chain of the deepest node (smallest
-    index among equals), the whole tree for a single chain."""
+def _runs_agree(w, T, cfgs, fused, paged, what, check_mask):
+    """Two runs of the same T steps with Runner options cfgs[0] and cfgs[1]: after every
+    step acceptance, commit log, status, attention, counts, open sums, tails and every
+    committed pool entry are the same bits, and both match the oracle."""
     import torch
-    w, T = IN_PLACE[name]
-    _say(f"in-place chain {name} fused={fused} paged={paged}: {T} steps")
     caps = pooled_caps(w, T * w.D + 8)
     page_seed = 21 if paged else None
     runs = []
-    for in_place in (False, True):
+    for cfg in cfgs:
         dst = device_state(w, caps, poison=True, page_seed=page_seed, spare_pages=3 if paged else 0)
-        runs.append((dst, Runner(dst, w.D, w.Hq, in_place=in_place)))
+        runs.append((dst, Runner(dst, w.D, w.Hq, **cfg)))
     (da, ra), (db, rb) = runs
     ost = oracle_state(w, caps)
     for t in range(T):
@@ -245,15 +238,16 @@ def test_in_place_chain_equals_copy_path(name, fused, paged):
             r.step(x, fused=fused)
         torch.cuda.synchronize()
         ref = oracle.step(ost, s.parents, s.draft, s.target, h.q, h.kt, h.vt)
-        # the in-place mask: the chain of the deepest node, smallest index among equals
-        anc, depth, _ = oracle.build_plan(s.parents)
-        want = []
-        for b in range(w.B):
-            leaf = int(np.lexsort((np.arange(w.D), -depth[b]))[0])
-            want.append(int(oracle.anc_to_bits(anc[b, leaf][None])[0]))
-        assert (rb.sc.in_place.cpu().numpy().view(np.uint64) == np.array(want, dtype=np.uint64)).all(), f"step {t}"
-        if w.topk == 1:
-            assert all(v == (1 << w.D) - 1 for v in want)
+        if check_mask:
+            # the in-place mask: the chain of the deepest node, smallest index among equals
+            anc, depth, _ = oracle.build_plan(s.parents)
+            want = []
+            for b in range(w.B):
+                leaf = int(np.lexsort((np.arange(w.D), -depth[b]))[0])
+                want.append(int(oracle.anc_to_bits(anc[b, leaf][None])[0]))
+            assert (rb.sc.in_place.cpu().numpy().view(np.uint64) == np.array(want, dtype=np.uint64)).all(), f"step {t}"
+            if w.topk == 1:
+                assert all(v == (1 << w.D) - 1 for v in want)
         for name_ in ("m", "path", "bonus", "log", "err"):
             assert torch.equal(getattr(ra, name_), getattr(rb, name_)), f"step {t} {name_}"
         assert torch.equal(_bits(ra.out), _bits(rb.out)), f"step {t} attention"
@@ -261,7 +255,8 @@ def test_in_place_chain_equals_copy_path(name, fused, paged):
         assert torch.equal(da.P, db.P)
         for l in range(len(w.levels)):
             assert torch.equal(da.n[l], db.n[l])
-            assert torch.equal(da.open_k[l], db.open_k[l]) and torch.equal(da.open_v[l], db.open_v[l])
+            assert torch.equal(da.open_k[l], db.open_k[l]) and torch.equal(da.open_v[l], db.open_v[l]), \
+                f"step {t} level {l} open sums"
             n = da.n[l].cpu().numpy()
             ka, kb = da.logical_k(l), db.logical_k(l)
             va = tv_untile(da.logical_vt(l))
@@ -272,7 +267,41 @@ def test_in_place_chain_equals_copy_path(name, fused, paged):
         if da.tail_k is not None:
             assert torch.equal(_bits(da.tail_k), _bits(db.tail_k)) and torch.equal(_bits(da.tail_v), _bits(db.tail_v))
         ost = ref.state
-    compare_state(db, ost, w.dtype, f"{name} in place, final state")
+    compare_state(db, ost, w.dtype, f"{what}, final state")
+
+
+@pytest.mark.parametrize("name,fused,paged", [(n, False, False) for n in IN_PLACE] +
+                         [("bf16_tree_c4_c128", True, False), ("bf16_chain_c4_c128", False, True)])
+def test_in_place_chain_equals_copy_path(name, fused, paged):
+    """The refresh skip (TSD-V4 §4.3): with scratch.in_place the verify writes the deepest
+    chain's closing entries straight into their pool slots and the refresh copies only the
+    other accepted nodes' entries.  Step after step the run matches the run without it bit
+    for bit -- acceptance, commit log, status, counts, open sums, tails and every committed
+    pool entry -- and the oracle; in_place[b] is the chain of the deepest node (smallest
+    index among equals), the whole tree for a single chain."""
+    w, T = IN_PLACE[name]
+    _say(f"in-place chain {name} fused={fused} paged={paged}: {T} steps")
+    _runs_agree(w, T, [dict(in_place=False), dict(in_place=True)], fused, paged, f"{name} in place", True)
+
+
+@pytest.mark.parametrize("name,deferred,fused,paged", [
+    ("bf16_tree_c4_c128", 2, False, False),   # the coarse level deferred, C128 crossings
+    ("bf16_chain_c4_c128", 2, False, False),  # a chain: level 0 in place, level 1 deferred
+    ("bf16_tree_c1_c4", 3, False, False),     # both levels: a block closes at every token
+    ("f32_chain_c2_c8", 3, True, False),      # fp32, acceptance and refresh in one launch
+    ("bf16_tree_c4_c128", 2, True, True),     # paged pools
+    ("f32_chain64_c1_c2", 3, False, False),   # 64 accepted tokens: path tokens in 8 batches
+])
+def test_deferred_levels_equal_scratch_path(name, deferred, fused, paged):
+    """Deferred levels (TSD-V4 §4.3: the coarse level's writes delayed and combined once the
+    accepted path is known): with scratch.deferred the verify builds no scratch states for
+    those levels and the refresh brings them up to date from the accepted path's tokens.
+    Step after step the state matches the run that builds every level's scratch states bit
+    for bit (open sums, every committed entry, counts, commit log), and the oracle."""
+    w, T = IN_PLACE[name] if name in IN_PLACE else FUSED[name]
+    _say(f"deferred levels {name} mask={deferred} fused={fused} paged={paged}: {T} steps")
+    _runs_agree(w, T, [dict(in_place=True), dict(in_place=True, deferred=deferred)], fused, paged,
+                f"{name} deferred {deferred}", False)
 
 
 def tv_untile(vt):

@@ -10,7 +10,12 @@
 // Every committed element is a bit copy: scratch entries of the path nodes that close a
 // block go to the next pool slots (except those the verify already wrote there: nodes of
 // the scratch pad's in-place chain, TSD-V4 §4.3's refresh skip), the path leaf's
-// open-block sums replace the open sums, path tokens extend the raw tail.  Counters (P,
+// open-block sums replace the open sums, path tokens extend the raw tail.  A level marked
+// in scratch.deferred (TSD-V4 §4.3: the coarse level's writes delayed and combined once the
+// accepted path is known) has no scratch states: its open sum and the entries the path
+// closes are computed here from the committed open sum and the path tokens, in path
+// order in fp32 with one rounding per entry -- the additions the scratch pad would have
+// made along the same chain, so the results are the same bits.  Counters (P,
 // n) are written after a barrier, once every thread of the sequence has read the old
 // values.  Rejected nodes are never read.
 #include "accept_path.h"
@@ -44,6 +49,21 @@ template <>
 struct Bits<float> {
   static __device__ __forceinline__ uint32_t ld(const float* p, size_t i) { return __float_as_uint(p[i]); }
   static __device__ __forceinline__ void st(float* p, size_t i, uint32_t v) { p[i] = __uint_as_float(v); }
+};
+
+// A storage element's bits widened to fp32, and an fp32 value rounded once (to nearest
+// even) to a storage element's bits.
+template <typename T>
+struct Wide;
+template <>
+struct Wide<uint16_t> {
+  static __device__ __forceinline__ float f(uint32_t v) { return bf16_bits_to_f32(v); }
+  static __device__ __forceinline__ uint32_t bits(float x) { return f32_to_bf16_bits(x); }
+};
+template <>
+struct Wide<float> {
+  static __device__ __forceinline__ float f(uint32_t v) { return __uint_as_float(v); }
+  static __device__ __forceinline__ uint32_t bits(float x) { return __float_as_uint(x); }
 };
 
 // Commits and tail tokens whose loads are issued together, ahead of any store (the
@@ -95,7 +115,9 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
     sh.it_j[i] = j;
     const int u = sh.pth[j * C + C - 1 - P];  // path node at the block's last position
     sh.it_u[i] = u;
-    if (!((in_place >> (u & 63)) & 1ull) || u < 0) sh.cp[atomicAdd(&sh.ncp, 1)] = i;  // not yet in its slot
+    // not yet in its slot (a deferred level's entries are computed below, not copied)
+    if (!((sc.deferred >> (l1 ? 1 : 0)) & 1u) && (!((in_place >> (u & 63)) & 1ull) || u < 0))
+      sh.cp[atomicAdd(&sh.ncp, 1)] = i;
     sh.it_tile0[i] = t0;
     sh.it_gstep[i] = tile_offset(paged, page, lv.cap, st.B, Hkv, d, b, 1, j >> 6) - t0;
   }
@@ -114,6 +136,7 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
       row[1] = sh.it_u[i];
     }
   const int leaf = sh.pth[m];
+  const bool def0 = L > 0 && (sc.deferred & 1u), def1 = L > 1 && (sc.deferred & 2u);
   // the finest level's raw tail: positions [t0, P2) come from the path; positions below
   // P keep their slot when no block closed (t_new == old start), when one closed t_new > P
   // and only path tokens remain
@@ -135,11 +158,11 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
     // uniform test (a missing item re-reads item 0), so no load waits for another; the
     // empty asm makes every load issue before the first store.
     float osk0 = 0.f, osv0 = 0.f, osk1 = 0.f, osv1 = 0.f;
-    if (L > 0) {
+    if (L > 0 && !def0) {
       osk0 = sc.open_k[0][(seq_rows + leaf) * HD + e];
       osv0 = sc.open_v[0][(seq_rows + leaf) * HD + e];
     }
-    if (L > 1) {
+    if (L > 1 && !def1) {
       osk1 = sc.open_k[1][(seq_rows + leaf) * HD + e];
       osv1 = sc.open_v[1][(seq_rows + leaf) * HD + e];
     }
@@ -174,6 +197,61 @@ __device__ __forceinline__ void refresh_body(int b, int D, const tv_state& st, c
           Bits<T>::st((T*)lv.k, tb + (size_t)(j & 63) * d + dd, ck[t]);
           Bits<T>::st((T*)lv.vt, tb + (size_t)dd * 64 + (j & 63), cv[t]);
         }
+    }
+    if (def0 || def1) {  // uniform: the deferred levels, from the path tokens
+      // the committed open sum counts only while the open block began before the path
+      float dk[2], dv[2];
+#pragma unroll
+      for (int l = 0; l < 2; ++l) {
+        const bool on = l == 0 ? def0 : def1;
+        const bool open = on && P % st.lvl[l].C != 0;
+        dk[l] = open ? st.lvl[l].open_k[(size_t)b * HD + e] : 0.f;
+        dv[l] = open ? st.lvl[l].open_v[(size_t)b * HD + e] : 0.f;
+      }
+      for (int t0 = 0; t0 <= m; t0 += kCommitBatch) {
+        uint32_t xk[kCommitBatch], xv[kCommitBatch];
+#pragma unroll
+        for (int t = 0; t < kCommitBatch; ++t) {  // a batch of path tokens, every load first
+          const size_t src = (seq_rows + sh.pth[t0 + t <= m ? t0 + t : t0]) * HD + e;
+          xk[t] = Bits<T>::ld(k_tree, src);
+          xv[t] = Bits<T>::ld(v_tree, src);
+        }
+        asm volatile("" ::"v"(xk[0]), "v"(xk[1]), "v"(xk[2]), "v"(xk[3]), "v"(xk[4]), "v"(xk[5]), "v"(xk[6]),
+                     "v"(xk[7]), "v"(xv[0]), "v"(xv[1]), "v"(xv[2]), "v"(xv[3]), "v"(xv[4]), "v"(xv[5]), "v"(xv[6]),
+                     "v"(xv[7]));
+#pragma unroll
+        for (int t = 0; t < kCommitBatch; ++t) {
+          if (t0 + t > m) break;  // uniform
+          const float fk = Wide<T>::f(xk[t]), fv = Wide<T>::f(xv[t]);
+          const int pos = P + t0 + t;
+#pragma unroll
+          for (int l = 0; l < 2; ++l) {
+            if (!(l == 0 ? def0 : def1)) continue;
+            dk[l] += fk;
+            dv[l] += fv;
+            const int C = st.lvl[l].C;
+            if ((pos + 1) % C == 0) {  // uniform: the block closes here, its entry is committed
+              const int j = pos / C;
+              const int i = (l ? nc[0] : 0) + (j - j0[l]);  // its listed block
+              const tv_level& lv = l ? st.lvl[1] : st.lvl[0];
+              const size_t tb = sh.it_tile0[i] + (size_t)g * sh.it_gstep[i];
+              const float cf = (float)C;
+              Bits<T>::st((T*)lv.k, tb + (size_t)(j & 63) * d + dd, Wide<T>::bits(dk[l] / cf));
+              Bits<T>::st((T*)lv.vt, tb + (size_t)dd * 64 + (j & 63), Wide<T>::bits(dv[l] / cf));
+              dk[l] = 0.f;
+              dv[l] = 0.f;
+            }
+          }
+        }
+      }
+      if (def0) {
+        osk0 = dk[0];
+        osv0 = dv[0];
+      }
+      if (def1) {
+        osk1 = dk[1];
+        osv1 = dv[1];
+      }
     }
     if (L > 0) {
       st.lvl[0].open_k[(size_t)b * HD + e] = osk0;

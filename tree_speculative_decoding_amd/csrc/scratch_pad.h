@@ -27,7 +27,8 @@
 // the device has room for them beside the stream.  The tree's depths are in LDS; thread t
 // takes the four consecutive elements 4t .. 4t+3 of the node's Hkv*d row (per pass of
 // 1024) and walks the node's chain once for every level, issuing the K and V loads of up
-// to eight chain nodes before adding them in chain order.
+// to eight chain nodes before adding them in chain order.  Levels marked in
+// scratch.deferred are skipped (no scratch states, no in-place writes).
 #pragma once
 #include "tv_common.h"
 
@@ -135,7 +136,8 @@ __device__ __forceinline__ void scratch_node(const AttnArgs& a, int b, int i, Sc
 
   using R = QuadRaw<T>;
   static_assert(TV_MAX_LEVELS == 2, "two levels: the sums below are named per level");
-  const bool lv1 = a.n_levels > 1;
+  // (a deferred level gets no scratch states: the refresh brings it up to date instead)
+  const bool lv1 = a.n_levels > 1 && !((a.scratch.deferred >> 1) & 1u);
   for (int e = 4 * tid; e < HD; e += 4 * 256) {
     // the open sums (level 0's address where level 1 is absent) and the chain's first
     // batch, loaded unconditionally and held as raw bits until every load is out (a
@@ -191,7 +193,7 @@ __device__ __forceinline__ void scratch_node(const AttnArgs& a, int b, int i, Sc
     } while (mm != 0ull);
 #pragma unroll
     for (int l = 0; l < TV_MAX_LEVELS; ++l) {
-      if (l >= a.n_levels) continue;
+      if (l >= a.n_levels || ((a.scratch.deferred >> l) & 1u)) continue;
       const float4 ks = sel4(l != 0, sk1, sk0), vs = sel4(l != 0, sv1, sv0);  // (l is a constant here)
       const int C = a.C[l];
       const size_t dst = ((size_t)b * a.D + i) * HD + e;

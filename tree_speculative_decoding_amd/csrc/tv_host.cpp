@@ -74,6 +74,13 @@ tv_status check_state(const tv_state* st) {
   return ok();
 }
 
+// Levels marked deferred must exist.
+tv_status check_deferred(const tv_scratch* sc, const tv_state* st) {
+  if ((sc->deferred >> st->n_levels) != 0u)
+    return fail(TV_EINVAL, "scratch.deferred = 0x%x marks levels beyond n_levels = %d", sc->deferred, st->n_levels);
+  return ok();
+}
+
 // compute units of the current device (asked once per device)
 int device_cus() {
   constexpr int kMaxDevices = 64;
@@ -244,8 +251,13 @@ tv_status run_attn(int D, int anc_ld, int Hq, const void* q, const void* k_tree,
   if (scratch != nullptr && !depth) return fail(TV_EINVAL, "the scratch pad needs depth");
   if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out))
     return fail(TV_EINVAL, "q, k_tree, v_tree and out must be 16-byte aligned");
+  if (scratch != nullptr) {
+    tv_status sd = check_deferred(scratch, st);
+    if (sd != TV_OK) return sd;
+  }
   if (scratch != nullptr)
     for (int l = 0; l < st->n_levels; ++l) {
+      if ((scratch->deferred >> l) & 1u) continue;  // no scratch states for this level
       if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
         return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
       if (!aligned16(scratch->entry_k[l]) || !aligned16(scratch->entry_v[l]) || !aligned16(scratch->open_k[l]) ||
@@ -430,8 +442,11 @@ TV_API tv_status tv_refresh_state(int D, const tv_state* st, const tv_scratch* s
   tv_scratch sc{};
   if (st->n_levels > 0) {
     if (scratch == nullptr) return fail(TV_EINVAL, "scratch is NULL");
+    s = check_deferred(scratch, st);
+    if (s != TV_OK) return s;
     for (int l = 0; l < st->n_levels; ++l)
-      if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
+      if (!((scratch->deferred >> l) & 1u) &&
+          (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l]))
         return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
     sc = *scratch;
   }
@@ -454,8 +469,11 @@ TV_API tv_status tv_accept_refresh(int D, const tv_state* st, const tv_scratch* 
   tv_scratch sc{};
   if (st->n_levels > 0) {
     if (scratch == nullptr) return fail(TV_EINVAL, "scratch is NULL");
+    s = check_deferred(scratch, st);
+    if (s != TV_OK) return s;
     for (int l = 0; l < st->n_levels; ++l)
-      if (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l])
+      if (!((scratch->deferred >> l) & 1u) &&
+          (!scratch->entry_k[l] || !scratch->entry_v[l] || !scratch->open_k[l] || !scratch->open_v[l]))
         return fail(TV_EINVAL, "scratch level %d has a NULL pointer", l);
     sc = *scratch;
   }

@@ -51,7 +51,7 @@ class TvState(ctypes.Structure):
 class TvScratch(ctypes.Structure):
     _fields_ = [("entry_k", ctypes.c_void_p * TV_MAX_LEVELS), ("entry_v", ctypes.c_void_p * TV_MAX_LEVELS),
                 ("open_k", ctypes.c_void_p * TV_MAX_LEVELS), ("open_v", ctypes.c_void_p * TV_MAX_LEVELS),
-                ("in_place", ctypes.c_void_p)]
+                ("in_place", ctypes.c_void_p), ("deferred", ctypes.c_uint32)]
 
 
 _lib = None
@@ -297,16 +297,20 @@ class DeviceState:
 class DeviceScratch:
     """Device tensors of a tv_scratch for B sequences of D nodes.  in_place=True gives the
     struct its in_place mask array (the verify writes one chain's entries straight into the
-    pools and the refresh skips them); False leaves it NULL (every entry is copied)."""
+    pools and the refresh skips them); False leaves it NULL (every entry is copied).
+    deferred: mask of the levels the refresh brings up to date from the accepted path
+    (no scratch tensors are allocated for them; their pointers stay NULL)."""
 
     def __init__(self, B: int, D: int, Hkv: int, d: int, dtype: str, n_levels: int, device="cuda",
-                 in_place: bool = True):
+                 in_place: bool = True, deferred: int = 0):
         td = torch_dtype(dtype)
-        self.entry_k = [torch.zeros(B, D, Hkv, d, dtype=td, device=device) for _ in range(n_levels)]
-        self.entry_v = [torch.zeros(B, D, Hkv, d, dtype=td, device=device) for _ in range(n_levels)]
-        self.open_k = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
-        self.open_v = [torch.zeros(B, D, Hkv, d, dtype=torch.float32, device=device) for _ in range(n_levels)]
+        mk = lambda l, t: None if (deferred >> l) & 1 else torch.zeros(B, D, Hkv, d, dtype=t, device=device)
+        self.entry_k = [mk(l, td) for l in range(n_levels)]
+        self.entry_v = [mk(l, td) for l in range(n_levels)]
+        self.open_k = [mk(l, torch.float32) for l in range(n_levels)]
+        self.open_v = [mk(l, torch.float32) for l in range(n_levels)]
         self.in_place = torch.zeros(B, dtype=torch.int64, device=device) if in_place else None
+        self.deferred = deferred
         self._struct = None
 
     def struct(self) -> TvScratch:
@@ -317,12 +321,14 @@ class DeviceScratch:
 
     def _make_struct(self) -> TvScratch:
         s = TvScratch()
+        ptr = lambda t: t.data_ptr() if t is not None else None
         for l in range(len(self.entry_k)):
-            s.entry_k[l] = self.entry_k[l].data_ptr()
-            s.entry_v[l] = self.entry_v[l].data_ptr()
-            s.open_k[l] = self.open_k[l].data_ptr()
-            s.open_v[l] = self.open_v[l].data_ptr()
-        s.in_place = self.in_place.data_ptr() if self.in_place is not None else None
+            s.entry_k[l] = ptr(self.entry_k[l])
+            s.entry_v[l] = ptr(self.entry_v[l])
+            s.open_k[l] = ptr(self.open_k[l])
+            s.open_v[l] = ptr(self.open_v[l])
+        s.in_place = ptr(self.in_place)
+        s.deferred = self.deferred
         return s
 
 
