@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-in-place", action="store_true",
                     help="scratch pad without the in-place chain: the refresh copies every committed entry")
+    ap.add_argument("--defer-coarse", action="store_true",
+                    help="the coarsest level gets no scratch states; the refresh updates it from the accepted path")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the draft-tree, draft-attention and paged-pool measurements (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
@@ -430,7 +432,7 @@ def pooled_state(w, caps, draw_seqs=None):
 class StepRunner:
     """Per-step buffers of one (B, D, Hq) shape and the four calls of one step on `stream`."""
 
-    def __init__(self, w, st, parts: int, stream, in_place: bool = True):
+    def __init__(self, w, st, parts: int, stream, in_place: bool = True, deferred: int = 0):
         import torch
         import tree_speculative_decoding_amd as tv
         B, D, Hq, Hkv, d, dev = st.B, w.D, w.Hq, w.Hkv, w.d, "cuda"
@@ -445,7 +447,7 @@ class StepRunner:
         self.path = torch.zeros(B, D, dtype=torch.int32, device=dev)
         self.bonus = torch.zeros(B, dtype=torch.int32, device=dev)
         self.log = torch.zeros(B, len(w.levels), D, 2, dtype=torch.int32, device=dev)
-        self.sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels), in_place=in_place)
+        self.sc = tv.DeviceScratch(B, D, Hkv, d, w.dtype, len(w.levels), in_place=in_place, deferred=deferred)
         self.ws = torch.empty(tv.tv_verify_attn_workspace_bytes(D, Hq, st, parts) // 4 + 64, dtype=torch.float32,
                               device=dev)
 
@@ -592,7 +594,8 @@ def main():
     states = [pooled_state(w.with_(B=B * n_rot), caps, range(r * B, (r + 1) * B)) for r in range(n_rot)]
     st = states[0]
     stream = torch.cuda.current_stream()
-    runner = StepRunner(w, st, args.parts, stream, in_place=not args.no_in_place)
+    deferred = (1 << (len(w.levels) - 1)) if args.defer_coarse and len(w.levels) > 1 else 0
+    runner = StepRunner(w, st, args.parts, stream, in_place=not args.no_in_place, deferred=deferred)
     sets = [runner.inputs(t) for t in range(N_INPUT_SETS)]
     saved_all = [snapshot(x) for x in states]
     torch.cuda.synchronize()
@@ -634,6 +637,7 @@ def main():
                    "prefix_tokens": w.P, "levels": list(w.levels), "tree": w.spec_name,
                    "p_agree": w.p_agree, "prefix_workgroups": args.parts or "auto",
                    "refresh_skip": "off" if args.no_in_place else "in-place chain",
+                   "coarse_level": "deferred to the refresh" if deferred else "scratch pad",
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name),
