@@ -552,8 +552,9 @@ def pct(xs, q) -> float:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU "
-              "in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the verify path is "
+              "implemented and measured on a single GPU (every call is independent per sequence, so "
+              "sequences would be split over GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:
